@@ -1,0 +1,198 @@
+// fa_api.hip — the C ABI declared in include/fa.h: argument validation (host only, before any
+// HIP call), instance selection, launches on the caller's stream, status mapping.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+// Shapes: sizes non-negative, head counts positive, element counts within int64 and the grid.
+fa_status check_shape(int B, int Hq, int Hkv, int N, int d) {
+    if (B < 0 || N < 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return FA_ERR_SHAPE;
+    const long double elems = (long double)B * Hq * N * d;
+    if (elems > 9.0e18L) return FA_ERR_SHAPE;
+    // 1-D grids: tiles x heads must fit an unsigned grid dimension.
+    if ((long double)B * Hq * ((N + 63) / 64) > 4.0e9L) return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_GQA;
+    return FA_OK;
+}
+
+fa_status check_scale(float scale) {
+    return (isfinite(scale) && scale > 0.f) ? FA_OK : FA_ERR_SCALE;
+}
+
+fa_status device_ready() {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();   // clear the sticky error so later calls are not confused
+        return FA_ERR_DEVICE;
+    }
+    return FA_OK;
+}
+
+fa_status launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_str(int s) {
+    switch (s) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL: return "a required pointer is NULL";
+        case FA_ERR_SHAPE: return "invalid shape (negative size, zero heads or size overflow)";
+        case FA_ERR_DTYPE: return "unsupported dtype for this entry point";
+        case FA_ERR_HEADDIM: return "unsupported head dimension for this dtype";
+        case FA_ERR_GQA: return "Hq is not a multiple of Hkv";
+        case FA_ERR_SCALE: return "scale must be finite and > 0";
+        case FA_ERR_ALIGN: return "misaligned pointer";
+        case FA_ERR_WORKSPACE: return "workspace missing or too small";
+        case FA_ERR_DEVICE: return "no HIP device available";
+        case FA_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char* fa_fwd_kernel_name(int d, int causal, int has_key_lens, fa_dtype dtype) {
+    (void)has_key_lens;   // key lengths are a runtime argument of every instance
+    if (dtype == FA_BF16) {
+        if (d == 128) return causal ? "fwd_bf16<d128,causal>" : "fwd_bf16<d128>";
+        if (d == 64) return causal ? "fwd_bf16<d64,causal>" : "fwd_bf16<d64>";
+        return "none";
+    }
+    if (dtype == FA_F32 && d >= 1 && d <= 128)
+        return d <= 32 ? "fwd_f32<dmax32>" : d <= 64 ? "fwd_f32<dmax64>" : "fwd_f32<dmax128>";
+    return "none";
+}
+
+const char* fa_bwd_kernel_name(int d, int causal, int has_key_lens, fa_dtype dtype) {
+    (void)has_key_lens;
+    if (dtype != FA_BF16) return "none";
+    if (d == 128) return causal ? "bwd_main_bf16<d128,causal>" : "bwd_main_bf16<d128>";
+    if (d == 64) return causal ? "bwd_main_bf16<d64,causal>" : "bwd_main_bf16<d64>";
+    return "none";
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 const int32_t* key_lens, int B, int Hq, int Hkv, int N, int d, float scale,
+                 int causal, fa_dtype dtype, void* stream) {
+    if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_DTYPE;
+    fa_status st = check_shape(B, Hq, Hkv, N, d);
+    if (st != FA_OK) return st;
+    if (dtype == FA_BF16 && d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (dtype == FA_F32 && d > 128) return FA_ERR_HEADDIM;
+    if ((st = check_scale(scale)) != FA_OK) return st;
+    if (B == 0 || N == 0) return FA_OK;   // empty problem: nothing to compute
+    if (!q || !k || !v || !o) return FA_ERR_NULL;
+    const uintptr_t a = dtype == FA_BF16 ? 16 : 4;
+    if (misaligned(q, a) || misaligned(k, a) || misaligned(v, a) || misaligned(o, a) ||
+        misaligned(lse, 4) || misaligned(key_lens, 4))
+        return FA_ERR_ALIGN;
+    if ((st = device_ready()) != FA_OK) return st;
+    fa::FwdParams p{q, k, v, o, lse, key_lens, B, Hq, Hkv, N, d, scale, causal ? 1 : 0};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return launched(dtype == FA_BF16 ? fa::launch_fwd_bf16(p, s) : fa::launch_fwd_f32(p, s));
+}
+
+size_t fa_bwd_workspace_size(int B, int Hq, int N, int d) {
+    if (B < 0 || Hq <= 0 || N < 0 || d <= 0) return 0;
+    return (size_t)B * (size_t)Hq * (size_t)N * sizeof(float);
+}
+
+static fa_status check_bwd_common(int B, int Hq, int Hkv, int N, int d, fa_dtype dtype,
+                                  size_t workspace_bytes, const void* workspace) {
+    if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_DTYPE;
+    fa_status st = check_shape(B, Hq, Hkv, N, d);
+    if (st != FA_OK) return st;
+    if (dtype != FA_BF16) return FA_ERR_DTYPE;        // fp32 backward is not provided
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (B == 0 || N == 0) return FA_OK;
+    if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, Hq, N, d)) return FA_ERR_WORKSPACE;
+    if (misaligned(workspace, 4)) return FA_ERR_ALIGN;
+    return FA_OK;
+}
+
+static fa_status validate_prep(const void* o, const void* dO, float* dq, const void* workspace,
+                               size_t workspace_bytes, int B, int Hq, int N, int d,
+                               fa_dtype dtype) {
+    fa_status st = check_bwd_common(B, Hq, Hq, N, d, dtype, workspace_bytes, workspace);
+    if (st != FA_OK || B == 0 || N == 0) return st;
+    if (!o || !dO || !dq) return FA_ERR_NULL;
+    if (misaligned(o, 16) || misaligned(dO, 16) || misaligned(dq, 16)) return FA_ERR_ALIGN;
+    return FA_OK;
+}
+
+static fa_status validate_main(const void* q, const void* k, const void* v, const void* dO,
+                               const float* lse, const int32_t* key_lens, float* dq, float* dk,
+                               float* dv, const void* workspace, size_t workspace_bytes, int B,
+                               int Hq, int Hkv, int N, int d, float scale, fa_dtype dtype) {
+    fa_status st = check_bwd_common(B, Hq, Hkv, N, d, dtype, workspace_bytes, workspace);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(scale)) != FA_OK) return st;
+    if (B == 0 || N == 0) return FA_OK;
+    if (!q || !k || !v || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(dO, 16) ||
+        misaligned(lse, 4) || misaligned(key_lens, 4) || misaligned(dq, 16) ||
+        misaligned(dk, 16) || misaligned(dv, 16))
+        return FA_ERR_ALIGN;
+    return FA_OK;
+}
+
+static fa::BwdParams bwd_params(const void* q, const void* k, const void* v, const void* o,
+                                const void* dO, const float* lse, const int32_t* key_lens,
+                                float* dq, float* dk, float* dv, const void* workspace, int B,
+                                int Hq, int Hkv, int N, int d, float scale, int causal) {
+    return fa::BwdParams{q, k, v, o, dO, lse, key_lens, dq, dk, dv,
+                         static_cast<float*>(const_cast<void*>(workspace)), B, Hq, Hkv, N, d,
+                         scale, causal ? 1 : 0};
+}
+
+fa_status fa_bwd_prep(const void* o, const void* dO, float* dq, void* workspace,
+                      size_t workspace_bytes, int B, int Hq, int N, int d, fa_dtype dtype,
+                      void* stream) {
+    fa_status st = validate_prep(o, dO, dq, workspace, workspace_bytes, B, Hq, N, d, dtype);
+    if (st != FA_OK || B == 0 || N == 0) return st;
+    if ((st = device_ready()) != FA_OK) return st;
+    fa::BwdParams p = bwd_params(nullptr, nullptr, nullptr, o, dO, nullptr, nullptr, dq, nullptr,
+                                 nullptr, workspace, B, Hq, Hq, N, d, 1.f, 0);
+    return launched(fa::launch_bwd_prep_bf16(p, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dO,
+                      const float* lse, const int32_t* key_lens, float* dq, float* dk, float* dv,
+                      const void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                      int N, int d, float scale, int causal, fa_dtype dtype, void* stream) {
+    fa_status st = validate_main(q, k, v, dO, lse, key_lens, dq, dk, dv, workspace,
+                                 workspace_bytes, B, Hq, Hkv, N, d, scale, dtype);
+    if (st != FA_OK || B == 0 || N == 0) return st;
+    if ((st = device_ready()) != FA_OK) return st;
+    fa::BwdParams p = bwd_params(q, k, v, nullptr, dO, lse, key_lens, dq, dk, dv, workspace, B,
+                                 Hq, Hkv, N, d, scale, causal);
+    return launched(fa::launch_bwd_main_bf16(p, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                 const float* lse, const int32_t* key_lens, float* dq, float* dk, float* dv,
+                 void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
+                 float scale, int causal, fa_dtype dtype, void* stream) {
+    // Validate everything both stages need before launching either.
+    fa_status st = validate_main(q, k, v, dO, lse, key_lens, dq, dk, dv, workspace,
+                                 workspace_bytes, B, Hq, Hkv, N, d, scale, dtype);
+    if (st != FA_OK || B == 0 || N == 0) return st;
+    if ((st = validate_prep(o, dO, dq, workspace, workspace_bytes, B, Hq, N, d, dtype)) != FA_OK)
+        return st;
+    if ((st = device_ready()) != FA_OK) return st;
+    fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, key_lens, dq, dk, dv, workspace, B, Hq,
+                                 Hkv, N, d, scale, causal);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = launched(fa::launch_bwd_prep_bf16(p, s))) != FA_OK) return st;
+    return launched(fa::launch_bwd_main_bf16(p, s));
+}
+
+}  // extern "C"

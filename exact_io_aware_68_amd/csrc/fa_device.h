@@ -1,0 +1,98 @@
+// fa_device.h — internal device helpers shared by the gfx950 attention kernels.
+//
+// Everything here is CDNA4-specific: 64-lane wavefronts, the double-rate bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16), the hardware base-2 exponential (v_exp_f32), the lane-half swap
+// (v_permlane32_swap_b32) and the packed fp32 -> bf16 round-to-nearest-even conversion
+// (v_cvt_pk_bf16_f32).
+//
+// MFMA 32x32x16 register layout used throughout (one wave, lane l, c = l % 32, h = l / 32):
+//   A (32 x 16): lane holds 8 values of row c, reduction slots (h, 0..7)
+//   B (16 x 32): lane holds 8 values of column c, reduction slots (h, 0..7)
+//   C (32 x 32): lane holds column c, register r is row 8*(r/4) + 4*h + (r%4)
+// A and B pair their reduction slots identically, so which reduction index sits in which slot is
+// ours to choose as long as both operands agree; the kernels exploit that to feed the C layout
+// of one product straight into the B operand of the next.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kPosInf = __builtin_huge_valf();
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x with the hardware instruction (inputs here are <= 0 or -inf; -inf gives 0).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value held by lane l ^ 32, combined with ours: permlane32_swap exchanges the upper half of its
+// first operand with the lower half of its second, so with both operands equal the pair holds
+// {ours, partner's} in some order on every lane.
+__device__ __forceinline__ float max_with_partner(float x) {
+    u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_partner(float x) {
+    u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 8 fp32 -> 8 bf16, round to nearest even (4 x v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3, float a4,
+                                            float a5, float a6, float a7) {
+    f32x8 v = {a0, a1, a2, a3, a4, a5, a6, a7};
+    return __builtin_convertvector(v, bf16x8);
+}
+__device__ __forceinline__ bf16x4 to_bf16x4(float a0, float a1, float a2, float a3) {
+    f32x4 v = {a0, a1, a2, a3};
+    return __builtin_convertvector(v, bf16x4);
+}
+
+// Two 8-byte halves -> one MFMA operand.
+__device__ __forceinline__ bf16x8 join(u32x2 lo, u32x2 hi) {
+    u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Transpose four rows of 8 bf16 (as 4 dwords each) into eight columns of 4 bf16 (as 2 dwords
+// each): col[e] = (r0[e], r1[e], r2[e], r3[e]).  v_perm_b32 picks 16-bit halves.
+__device__ __forceinline__ void transpose4x8(const u32x4 r[4], u32x2 col[8]) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        // low halves (even columns) and high halves (odd columns)
+        col[2 * w][0] = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x05040100u);
+        col[2 * w][1] = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x05040100u);
+        col[2 * w + 1][0] = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x07060302u);
+        col[2 * w + 1][1] = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x07060302u);
+    }
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// Workgroup order.  Workgroups are handed to the 8 XCDs round-robin by id; remapping so that
+// each XCD receives a contiguous range of logical indices keeps all tiles of one head on one XCD
+// (and its L2), so the K/V re-reads of neighbouring tiles hit in that L2.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblk) {
+    if ((nblk & 7) != 0) return bid;
+    return (bid & 7) * (nblk >> 3) + (bid >> 3);
+}
+
+}  // namespace fa

@@ -1,0 +1,136 @@
+/*
+ * fa.h — C ABI of the exact tiled softmax attention library for AMD MI355X (gfx950).
+ *
+ * The operation (tutorial page "Flash attention and efficient attention", section "The Standard
+ * Attention Problem"): S = Q K^T, P = softmax(scale * S) row by row, O = P V.  The forward pass
+ * follows the guide page ("FlashAttention", section "Tiling through SRAM"): a query tile stays on
+ * chip, key/value tiles stream through it, the softmax is carried online (tutorial page,
+ * "Derivation: Incremental Softmax", steps 1-3: running max, running sum, rescaled unnormalised
+ * output), and only O plus a little per-row softmax metadata reach memory.  That metadata is the
+ * natural-log log-sum-exp LSE_i = ln(sum_j exp(scale * s_ij)) of each row.  The backward pass
+ * (tutorial page, "Backward Pass: Recomputation"; guide page, same section as above) recomputes
+ * S and P tile by tile from Q, K, V and LSE instead of reading a stored N x N map.
+ *
+ * Masks (guide page, "Tiling through SRAM", causal masks / padding / grouped-query attention):
+ *   - causal: query i sees key j only when j <= i (top-left aligned, Nq = Nk = N);
+ *   - key_lens: keys j >= key_lens[b] are invisible to every query of batch b; query rows are
+ *     still computed; a row with no visible key gets O = 0, LSE = -inf and zero gradients;
+ *   - grouped-query heads: q-head h reads kv-head h / (Hq / Hkv) (contiguous groups).
+ *
+ * Layout: every tensor is contiguous, head dimension innermost ("BHND"):
+ *   q, o, dO : [B][Hq][N][d]        k, v : [B][Hkv][N][d]
+ *   lse      : [B][Hq][N] fp32      key_lens : [B] int32
+ *   dq       : [B][Hq][N][d] fp32   dk, dv : [B][Hkv][N][d] fp32 (summed over each group)
+ * All pointers are DEVICE pointers on the current HIP device, owned by the caller.  The library
+ * allocates no memory and keeps no mutable global state; calls are reentrant.
+ *
+ * Ordering: every call enqueues its kernels on `stream` (a hipStream_t passed as void*; NULL is
+ * the default stream) and returns without waiting.  Kernel faults surface at the caller's next
+ * synchronisation, as with any HIP launch.
+ *
+ * Errors: argument errors are detected on the host BEFORE any HIP call and returned as an
+ * fa_status; they are safe to test without a GPU.  FA_ERR_DEVICE means no usable HIP device;
+ * FA_ERR_LAUNCH means the launch itself failed.  No C++ exception crosses this interface.
+ *
+ * Supported instances:
+ *   - FA_BF16: d in {64, 128}; bf16 inputs and O, fp32 accumulation, MFMA contractions.
+ *   - FA_F32 : forward only, 1 <= d <= 128; fp32 throughout.
+ *   - any N >= 0, B >= 0 (an empty problem returns FA_OK and launches nothing), Hq % Hkv == 0,
+ *     scale finite and > 0; key_lens values are clamped to [0, N] on the device.
+ *   - q, k, v, o, dO, dq, dk, dv 16-byte aligned (fp32 forward: q, k, v, o 4-byte aligned);
+ *     lse, key_lens and workspace 4-byte aligned.
+ * Keys beyond key_lens[b] (and the padding rows of K and V) may hold any bits, NaN included;
+ * they never reach an output.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,      /* a required pointer is NULL                                      */
+    FA_ERR_SHAPE = 2,     /* B, Hq, Hkv or N negative, Hq or Hkv zero, or a size overflows    */
+    FA_ERR_DTYPE = 3,     /* unknown dtype, or a dtype this entry point does not support      */
+    FA_ERR_HEADDIM = 4,   /* d outside the supported set for the dtype                        */
+    FA_ERR_GQA = 5,       /* Hq is not a multiple of Hkv                                      */
+    FA_ERR_SCALE = 6,     /* scale not finite or not > 0                                      */
+    FA_ERR_ALIGN = 7,     /* a pointer is misaligned                                          */
+    FA_ERR_WORKSPACE = 8, /* workspace missing or smaller than fa_bwd_workspace_size()        */
+    FA_ERR_DEVICE = 9,    /* no HIP device available                                          */
+    FA_ERR_LAUNCH = 10    /* the kernel launch failed                                         */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+/*
+ * Forward: O = softmax(scale * Q K^T, masked) V and, if lse != NULL, the per-row natural-log
+ * log-sum-exp.  Inputs: q [B][Hq][N][d], k, v [B][Hkv][N][d] in `dtype`; key_lens NULL means
+ * every batch has N keys.  Outputs: o [B][Hq][N][d] in `dtype` (bf16 rounded to nearest even),
+ * lse [B][Hq][N] fp32 (may be NULL: O only).
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 const int32_t* key_lens, int B, int Hq, int Hkv, int N, int d, float scale,
+                 int causal, fa_dtype dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs: one fp32 per query row (D_i = sum_c dO_ic O_ic),
+ * i.e. B * Hq * N * 4 — linear in N, never N^2.  Returns 0 for an invalid shape.
+ */
+size_t fa_bwd_workspace_size(int B, int Hq, int N, int d);
+
+/*
+ * Backward by recomputation.  Inputs: q, k, v as in fa_fwd; o and lse exactly as fa_fwd wrote
+ * them; dO [B][Hq][N][d] in `dtype`.  Outputs (fp32, overwritten): dq [B][Hq][N][d],
+ * dk, dv [B][Hkv][N][d] — gradients of sum(O * dO) with respect to Q, K, V, where dK and dV of a
+ * kv-head are summed over the q-heads of its group, and keys at or beyond key_lens[b] get zero.
+ * workspace: device memory of at least fa_bwd_workspace_size() bytes, contents ignored.
+ * Only FA_BF16 with d in {64, 128} is supported.  dq is accumulated with fp32 atomics, so its
+ * low-order bits may vary from run to run; dk, dv and the forward are bitwise reproducible.
+ * Equivalent to fa_bwd_prep followed by fa_bwd_main on the same stream.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                 const float* lse, const int32_t* key_lens, float* dq, float* dk, float* dv,
+                 void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
+                 float scale, int causal, fa_dtype dtype, void* stream);
+
+/*
+ * First stage of fa_bwd: writes D_i = sum_c dO_ic O_ic (fp32) into the workspace and zeroes dq.
+ * Same argument conventions as fa_bwd.
+ */
+fa_status fa_bwd_prep(const void* o, const void* dO, float* dq, void* workspace,
+                      size_t workspace_bytes, int B, int Hq, int N, int d, fa_dtype dtype,
+                      void* stream);
+
+/*
+ * Second stage of fa_bwd: recomputes S and P per tile and produces dq (accumulated into the
+ * zeroed dq), dk and dv.  Requires fa_bwd_prep's workspace and zeroed dq, earlier on `stream`.
+ */
+fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dO,
+                      const float* lse, const int32_t* key_lens, float* dq, float* dk, float* dv,
+                      const void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                      int N, int d, float scale, int causal, fa_dtype dtype, void* stream);
+
+/* Name of the kernel instance fa_fwd / fa_bwd_main would launch for these arguments
+ * ("none" if unsupported); a static string, never freed. */
+const char* fa_fwd_kernel_name(int d, int causal, int has_key_lens, fa_dtype dtype);
+const char* fa_bwd_kernel_name(int d, int causal, int has_key_lens, fa_dtype dtype);
+
+/* Static description of a status code. */
+const char* fa_status_str(int status);
+
+/* FA_ABI_VERSION of the loaded library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,115 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol, and rejects
+bad arguments on the host before any HIP call (fake, never-dereferenced pointers)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_68_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, NULL, SHAPE, DTYPE, HEADDIM, GQA, SCALE, ALIGN, WORKSPACE, DEVICE, LAUNCH = range(11)
+A = 0x10000            # a 16-byte-aligned fake device address (never dereferenced here)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_workspace_size",
+            "fa_status_str", "fa_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define\s+FA_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert fa.fa_abi_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    for s in range(11):
+        assert fa.fa_status_str(s) and fa.fa_status_str(s) != "unknown status"
+    assert fa.fa_status_str(99) == "unknown status"
+
+
+def test_workspace_is_linear_in_N(lib):
+    assert fa.fa_bwd_workspace_size(2, 16, 4096, 128) == 2 * 16 * 4096 * 4
+    assert fa.fa_bwd_workspace_size(2, 16, 8192, 128) == 2 * fa.fa_bwd_workspace_size(2, 16, 4096, 128)
+    assert fa.fa_bwd_workspace_size(-1, 16, 8, 64) == 0
+
+
+def test_kernel_names(lib):
+    assert fa.fa_fwd_kernel_name(128, True, False, fa.FA_BF16) == "fwd_bf16<d128,causal>"
+    assert fa.fa_fwd_kernel_name(64, False, True, fa.FA_BF16) == "fwd_bf16<d64>"
+    assert fa.fa_fwd_kernel_name(96, False, False, fa.FA_BF16) == "none"
+    assert fa.fa_fwd_kernel_name(64, False, False, fa.FA_F32) == "fwd_f32<dmax64>"
+    assert fa.fa_bwd_kernel_name(128, True, False, fa.FA_BF16) == "bwd_main_bf16<d128,causal>"
+    assert fa.fa_bwd_kernel_name(128, True, False, fa.FA_F32) == "none"
+
+
+def fwd(lib, q=A, k=A, v=A, o=A, lse=A, kl=None, B=1, Hq=2, Hkv=1, N=8, d=64, scale=0.125,
+        causal=0, dtype=fa.FA_BF16):
+    return lib.fa_fwd(q, k, v, o, lse, kl, B, Hq, Hkv, N, d, ctypes.c_float(scale), causal,
+                      dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), DTYPE),
+    (dict(d=96), HEADDIM), (dict(d=32), HEADDIM), (dict(d=256, dtype=fa.FA_F32), HEADDIM),
+    (dict(Hq=3, Hkv=2), GQA), (dict(Hkv=0), SHAPE), (dict(N=-1), SHAPE), (dict(B=-2), SHAPE),
+    (dict(d=0), SHAPE),
+    (dict(scale=float("nan")), SCALE), (dict(scale=float("inf")), SCALE), (dict(scale=0.0), SCALE),
+    (dict(scale=-0.1), SCALE),
+    (dict(q=None), NULL), (dict(o=None), NULL),
+    (dict(k=A + 8), ALIGN), (dict(lse=A + 2), ALIGN), (dict(kl=A + 1), ALIGN),
+    (dict(B=0), OK), (dict(N=0), OK), (dict(B=0, q=None, o=None), OK),
+])
+def test_fwd_argument_errors_before_any_hip_call(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def test_fwd_f32_alignment_is_4_bytes(lib):
+    assert fwd(lib, q=A + 4, dtype=fa.FA_F32, d=33) != ALIGN
+    assert fwd(lib, q=A + 2, dtype=fa.FA_F32, d=33) == ALIGN
+
+
+def bwd(lib, q=A, k=A, v=A, o=A, do=A, lse=A, kl=None, dq=A, dk=A, dv=A, ws=A, wsb=1 << 20,
+        B=1, Hq=2, Hkv=1, N=8, d=128, scale=0.1, causal=1, dtype=fa.FA_BF16):
+    return lib.fa_bwd(q, k, v, o, do, lse, kl, dq, dk, dv, ws, wsb, B, Hq, Hkv, N, d,
+                      ctypes.c_float(scale), causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=fa.FA_F32), DTYPE), (dict(dtype=3), DTYPE), (dict(d=96), HEADDIM),
+    (dict(Hq=4, Hkv=3), GQA), (dict(ws=None), WORKSPACE), (dict(wsb=2 * 8 * 4 - 1), WORKSPACE),
+    (dict(scale=float("nan")), SCALE), (dict(do=None), NULL), (dict(lse=None), NULL),
+    (dict(dq=A + 4), ALIGN), (dict(dk=A + 8), ALIGN), (dict(ws=A + 2), ALIGN),
+    (dict(B=0, ws=None), OK),
+])
+def test_bwd_argument_errors_before_any_hip_call(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def _gpu_present():
+    import torch
+    return torch.cuda.is_available()
+
+
+@pytest.mark.skipif(_gpu_present(), reason="fake pointers must never reach a real GPU")
+def test_valid_call_without_device_reports_device_error(lib):
+    assert fwd(lib) == DEVICE
+    assert bwd(lib) == DEVICE
+    assert fwd(lib, B=0) == OK              # empty problems never touch HIP at all

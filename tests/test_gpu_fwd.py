@@ -1,0 +1,173 @@
+"""GPU parity of fa_fwd (through the C ABI) against the fp64 oracle on the same inputs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_68_amd as fa
+import fa_inputs as fi
+from oracle import attn_fwd, attn_fwd_rows
+from tests._parity import (TOL_BF16_MAX, TOL_BF16_MEAN, TOL_F32, TOL_LSE, check_close, np64)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run_fwd(x, causal, want_lse=True):
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    kl = None if x.get("key_lens") is None else x["key_lens"].to(DEV)
+    o, lse = fa.fa_fwd(q, k, v, scale=x["scale"], causal=causal, key_lens=kl, want_lse=want_lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def gen(B, Hq, Hkv, N, d, dtype, seed, padded=False, std=1.0):
+    w = fi.Workload("t", B, Hq, Hkv, N, d, dtype, False, padded, False, std, seed)
+    return fi.make(w)
+
+
+# ------------------------------------------------------------------ fp32 instance
+
+def test_worked_example_fp32():
+    ex = fi.worked_example()
+    ex["scale"] = 1 / math.sqrt(2)
+    for causal in (False, True):
+        o, lse = run_fwd(ex, causal)
+        O, LSE = attn_fwd(ex["q"], ex["k"], ex["v"], ex["scale"], causal)
+        check_close("O", np64(o), O, TOL_F32)
+        check_close("LSE", np64(lse), LSE, TOL_F32)
+    o, _ = run_fwd(ex, False)
+    np.testing.assert_allclose(np64(o)[0, 0, 0], [0.8302385, 1.1697615], atol=1e-6)
+
+
+def test_c1_fp32_full():
+    x = fi.make(fi.WORKLOADS["c1"])
+    o, lse = run_fwd(x, False, want_lse=False)
+    assert lse is None
+    O, _ = attn_fwd(x["q"], x["k"], x["v"], x["scale"])
+    check_close("O", np64(o), O, TOL_F32)
+
+
+@pytest.mark.parametrize("d", [1, 37, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_ragged(d, causal):
+    x = gen(2, 4, 2, 150, d, "f32", 100 + d, padded=True)
+    o, lse = run_fwd(x, causal)
+    O, LSE = attn_fwd(x["q"], x["k"], x["v"], x["scale"], causal, x["key_lens"])
+    check_close("O", np64(o), O, TOL_F32)
+    check_close("LSE", np64(lse), LSE, TOL_F32)
+
+
+# ------------------------------------------------------------------ bf16 instances
+
+CASES = [  # (B, Hq, Hkv, N, d, causal, padded)
+    (2, 2, 2, 300, 64, False, False),
+    (2, 2, 2, 300, 128, False, False),
+    (2, 2, 2, 300, 64, True, False),
+    (2, 2, 2, 300, 128, True, False),
+    (2, 4, 2, 300, 128, True, True),
+    (3, 4, 1, 257, 64, True, True),
+    (2, 6, 3, 200, 128, False, True),
+    (1, 2, 2, 1, 128, True, False),
+    (1, 2, 2, 63, 64, False, False),
+    (1, 2, 1, 129, 128, True, False),
+    (1, 1, 1, 640, 128, True, False),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,padded", CASES)
+def test_bf16_parity_small(B, Hq, Hkv, N, d, causal, padded):
+    x = gen(B, Hq, Hkv, N, d, "bf16", 1000 + N + d + 7 * Hq, padded)
+    print(f"\nfwd bf16 B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal}", flush=True)
+    o, lse = run_fwd(x, causal)
+    O, LSE = attn_fwd(x["q"], x["k"], x["v"], x["scale"], causal, x["key_lens"])
+    check_close("O", np64(o), O, TOL_BF16_MAX, TOL_BF16_MEAN)
+    check_close("LSE", np64(lse), LSE, TOL_LSE)
+
+
+def test_bf16_key_lengths_edge_values():
+    """key_lens of 0 (row has no key: O = 0, LSE = -inf), 1, a tile edge and N."""
+    x = gen(4, 2, 1, 200, 128, "bf16", 7)
+    x["key_lens"] = torch.tensor([0, 1, 64, 200], dtype=torch.int32)
+    for causal in (False, True):
+        o, lse = run_fwd(x, causal)
+        O, LSE = attn_fwd(x["q"], x["k"], x["v"], x["scale"], causal, x["key_lens"])
+        check_close("O", np64(o), O, TOL_BF16_MAX, TOL_BF16_MEAN)
+        check_close("LSE", np64(lse), LSE, TOL_LSE)
+        assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
+def test_nan_padding_never_reaches_outputs():
+    x = gen(2, 2, 2, 256, 64, "bf16", 8)
+    x["key_lens"] = torch.tensor([100, 193], dtype=torch.int32)
+    o_ref, l_ref = run_fwd(x, True)
+    for b, L in enumerate([100, 193]):
+        x["k"][b, :, L:] = float("nan")
+        x["v"][b, :, L:] = float("nan")
+    o, lse = run_fwd(x, True)
+    assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+
+
+def test_every_output_written_and_canaries_intact():
+    x = gen(2, 2, 1, 190, 128, "bf16", 9)
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    n_o, n_l = q.numel(), 2 * 2 * 190
+    ob = torch.full((n_o + 2048,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lb = torch.full((n_l + 2048,), float("nan"), dtype=torch.float32, device=DEV)
+    o = ob[1024:1024 + n_o].view(q.shape)
+    lse = lb[1024:1024 + n_l].view(2, 2, 190)
+    fa.fa_fwd(q, k, v, scale=x["scale"], causal=True, o=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    assert torch.isnan(ob[:1024]).all() and torch.isnan(ob[1024 + n_o:]).all()
+    assert torch.isnan(lb[:1024]).all() and torch.isnan(lb[1024 + n_l:]).all()
+
+
+def test_forward_is_bitwise_deterministic():
+    x = gen(2, 4, 2, 333, 128, "bf16", 10, padded=True)
+    o1, l1 = run_fwd(x, True)
+    o2, l2 = run_fwd(x, True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _sample_rows(w, n_rand, seed):
+    r = np.random.default_rng(seed)
+    picks = set()
+    for b in range(w.B):
+        for h in (0, w.Hq - 1):
+            for i in (0, 1, 63, 64, 127, 128, w.N // 2, w.N - 2, w.N - 1):
+                picks.add((b, h, i))
+    while len(picks) < n_rand + 36 * w.B:
+        picks.add((int(r.integers(w.B)), int(r.integers(w.Hq)), int(r.integers(w.N))))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+def test_full_size_workload_sampled_rows(name):
+    """Full-size workloads in the launch configuration the bench times; the oracle recomputes
+    sampled rows one by one (first, last, tile edges, random) and every row is checked for
+    finiteness."""
+    w = fi.WORKLOADS[name]
+    print(f"\nfull-size {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d}", flush=True)
+    x = fi.make(w)
+    o, lse = run_fwd(x, w.causal)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    picks = _sample_rows(w, 96, w.seed)
+    O, LSE = attn_fwd_rows(x["q"], x["k"], x["v"], x["scale"], w.causal, x["key_lens"], picks)
+    idx = tuple(torch.tensor(a) for a in zip(*picks))
+    check_close("O", np64(o[idx]), O, TOL_BF16_MAX, TOL_BF16_MEAN)
+    check_close("LSE", np64(lse[idx]), LSE, TOL_LSE)
+
+
+def test_c2_two_heads_in_full():
+    w = fi.WORKLOADS["c2"]
+    x = fi.make(w)
+    o, lse = run_fwd(x, False)
+    heads = [(0, 0), (3, 15)]
+    O, LSE = attn_fwd(x["q"], x["k"], x["v"], x["scale"], False, None, heads=heads)
+    for b, h in heads:
+        check_close("O", np64(o[b, h]), O[b, h], TOL_BF16_MAX, TOL_BF16_MEAN)
+        check_close("LSE", np64(lse[b, h]), LSE[b, h], TOL_LSE)
