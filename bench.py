@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Bench: exact tiled attention forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu-baseline]
+
+One step = one pass of the whole hot path over one batch of synthetic inputs already resident
+in HBM: fa_fwd (O and LSE) then fa_bwd (its two stages, fa_bwd_prep and fa_bwd_main), bf16 with
+fp32 accumulation.  The default workload is causal attention at B=2, H=16, N=8192, d=128 — the
+shape the headline metric is quoted on — with Q, K, V, dO drawn N(0,1)*0.5 from seed 3.
+
+Printed: ONE JSON line with whole-job TFLOP/s (forward 4*N^2*d*B*H halved for causal, backward
+2.5x that: five GEMM-shaped products instead of two), per-kernel HIP-event durations, the
+roofline of the dominant kernel and the fp64 CPU oracle timed on a bounded sample on the host's
+cores (a reported baseline, not a target).
+
+Also: --copy-calib runs a plain device copy of known size, the reference point that scales the
+rocprofv3 FETCH_SIZE / WRITE_SIZE counters into bytes.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+KERNEL_SRC = {                 # kernel -> source file whose hash guards stored counter data
+    "fwd_bf16": "exact_io_aware_68_amd/csrc/fa_fwd_bf16.hip",
+    "bwd_prep": "exact_io_aware_68_amd/csrc/fa_bwd_bf16.hip",
+    "bwd_main": "exact_io_aware_68_amd/csrc/fa_bwd_bf16.hip",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+# ------------------------------------------------------------------ work and byte models
+
+def fwd_flops(B, Hq, N, d, causal):
+    """Matmul flops of the forward: 4 N^2 d per head (QK^T and PV), halved when causal."""
+    f = 4.0 * N * N * d * B * Hq
+    return f / 2 if causal else f
+
+
+def bwd_flops(B, Hq, N, d, causal):
+    """Backward: recompute S, then dV, dP, dK, dQ: five products of the forward's size."""
+    return 2.5 * fwd_flops(B, Hq, N, d, causal)
+
+
+def fwd_bytes_compulsory(B, Hq, Hkv, N, d, elem=2):
+    """Tiled IO count of the forward: read Q, K, V once, write O and the fp32 LSE once."""
+    return (2 * B * Hq * N * d + 2 * B * Hkv * N * d) * elem + B * Hq * N * 4
+
+
+def bwd_bytes_compulsory(B, Hq, Hkv, N, d, elem=2):
+    """Backward: read Q, K, V, O, dO (bf16), LSE; write+read D; write fp32 dQ, dK, dV."""
+    reads = (3 * B * Hq * N * d + 2 * B * Hkv * N * d) * elem + B * Hq * N * 4
+    d_rw = 2 * B * Hq * N * 4
+    writes = (B * Hq * N * d + 2 * B * Hkv * N * d) * 4
+    return reads + d_rw + writes
+
+
+def naive_bytes(B, Hq, N, elem=2):
+    """Naive attention's score traffic alone: write S, read S, write P, read P (elem bytes)."""
+    return 4 * N * N * elem * B * Hq
+
+
+def noreuse_tiled_bytes(B, Hq, N, d, Br=128, elem=2, causal=False):
+    """Tiled attention with no on-chip reuse of K/V across query tiles: every q-tile re-reads
+    the K and V it needs (half of them on average when causal), plus Q and O once."""
+    ntiles = -(-N // Br)
+    kv = 2 * N * d * elem * ntiles * (0.5 if causal else 1.0)
+    return B * Hq * (kv + 2 * N * d * elem)
+
+
+# ------------------------------------------------------------------ helpers
+
+def _src_hash(path):
+    return hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload):
+    """Measured HBM bytes per launch from committed rocprofv3 counter summaries, or None when
+    absent or taken on a different kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+        e = t["kernels"][f"{kernel}@{workload}"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if e.get("src_hash") != _src_hash(KERNEL_SRC[kernel]):
+        return None
+    return e["bytes_per_launch"]
+
+
+def cpu_baseline(x, w, budget_s=20.0):
+    """Time the fp64 oracle (as written, untuned) forward + backward on whole heads of the same
+    workload, as many as fit the time budget (at least one)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attn_bwd, attn_fwd
+    heads = []
+    t0 = time.perf_counter()
+    g = w.Hq // w.Hkv
+    for b in range(w.B):
+        for hkv in range(w.Hkv):
+            sl = slice(hkv * g, (hkv + 1) * g)
+            q, k, v, do = (x[n][b:b + 1, s] for n, s in
+                           (("q", sl), ("k", slice(hkv, hkv + 1)), ("v", slice(hkv, hkv + 1)),
+                            ("do", sl)))
+            attn_fwd(q, k, v, x["scale"], w.causal)
+            attn_bwd(q, k, v, do, x["scale"], w.causal)
+            heads.append((b, hkv))
+            if time.perf_counter() - t0 > budget_s / 2:
+                break
+        if time.perf_counter() - t0 > budget_s / 2:
+            break
+    dt = time.perf_counter() - t0
+    nq = len(heads) * g
+    flops = fwd_flops(1, nq, w.N, w.d, w.causal) + bwd_flops(1, nq, w.N, w.d, w.causal)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle fwd+bwd on {nq} of {w.B * w.Hq} heads "
+                      f"(N={w.N}, d={w.d}, causal={w.causal}) in {dt:.1f} s; "
+                      f"host affinity {len(os.sched_getaffinity(0))} cpus"}
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device copy of known size for counter calibration (reads and writes nbytes)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--only", choices=["fwd", "bwd", "both"], default="both")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the attention path is "
+              "built and measured on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calib:
+        copy_calibration()
+        return
+
+    import torch
+
+    import exact_io_aware_68_amd as fa
+    import fa_inputs as fi
+
+    w = fi.WORKLOADS[args.workload]
+    x = fi.make(w, want_do=True)
+    dev = "cuda:0"
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    kl = None if x["key_lens"] is None else x["key_lens"].to(dev)
+    sc, causal = x["scale"], w.causal
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.Hq, w.N, w.d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    do_fwd = args.only in ("fwd", "both")
+    do_bwd = args.only in ("bwd", "both")
+    if do_bwd and not do_fwd:
+        fa.fa_fwd(q, k, v, scale=sc, causal=causal, key_lens=kl, o=o, lse=lse)
+
+    names = (["fwd_bf16"] if do_fwd else []) + (["bwd_prep", "bwd_main"] if do_bwd else [])
+    ev = {n: [] for n in names}
+
+    def step(record):
+        def mark(n, fn):
+            if record:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                ev[n].append((e0, e1))
+            else:
+                fn()
+        if do_fwd:
+            mark("fwd_bf16", lambda: fa.fa_fwd(q, k, v, scale=sc, causal=causal, key_lens=kl,
+                                               o=o, lse=lse))
+        if do_bwd:
+            mark("bwd_prep", lambda: fa.fa_bwd_prep(o, do, dq, ws))
+            mark("bwd_main", lambda: fa.fa_bwd_main(q, k, v, do, lse, dq, dk, dv, ws, scale=sc,
+                                                    causal=causal, key_lens=kl))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    kern_ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in names}
+
+    ff = fwd_flops(w.B, w.Hq, w.N, w.d, causal) if do_fwd else 0.0
+    bf = bwd_flops(w.B, w.Hq, w.N, w.d, causal) if do_bwd else 0.0
+    value = (ff + bf) / (ms_step * 1e-3) / 1e12
+    flops_of = {"fwd_bf16": ff, "bwd_main": bf, "bwd_prep": 0.0}
+    # dominant kernel: the one with the most time per step
+    dom = max(names, key=lambda n: kern_ms[n])
+    tr = stored_traffic(dom, args.workload)
+    if dom == "bwd_prep":
+        byt = bwd_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d)
+        ach = byt / (kern_ms[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": tr}
+    else:
+        ach = flops_of[dom] / (kern_ms[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": tr}
+    out = {
+        "metric": "attention fwd/bwd TFLOP/s + % bf16 MFMA peak, N=8192 d=128 causal",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"exact attention {args.only}, B={w.B} Hq={w.Hq} Hkv={w.Hkv} "
+                               f"N={w.N} d={w.d} causal={causal} "
+                               f"key_lens={'U[N/2,N]' if w.padded else 'none'}",
+                   "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "causal": causal,
+                   "seed": w.seed, "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels_ms": {n: round(t, 4) for n, t in kern_ms.items()},
+        "fwd": None if not do_fwd else {
+            "tflops": round(ff / (kern_ms["fwd_bf16"] * 1e-3) / 1e12, 2),
+            "pct_peak": round(100 * ff / (kern_ms["fwd_bf16"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "instance": fa.fa_fwd_kernel_name(w.d, causal, kl is not None, fa.FA_BF16),
+            "compulsory_bytes": fwd_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d),
+            "naive_score_bytes": naive_bytes(w.B, w.Hq, w.N),
+            "noreuse_tiled_bytes": noreuse_tiled_bytes(w.B, w.Hq, w.N, w.d, causal=causal),
+            "measured_bytes": stored_traffic("fwd_bf16", args.workload)},
+        "bwd": None if not do_bwd else {
+            "tflops": round(bf / ((kern_ms["bwd_main"] + kern_ms["bwd_prep"]) * 1e-3) / 1e12, 2),
+            "main_tflops": round(bf / (kern_ms["bwd_main"] * 1e-3) / 1e12, 2),
+            "instance": fa.fa_bwd_kernel_name(w.d, causal, kl is not None, fa.FA_BF16),
+            "compulsory_bytes": bwd_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d),
+            "measured_bytes": stored_traffic("bwd_main", args.workload)},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
