@@ -30,6 +30,13 @@ DEVICE_FLAGS = [
 ]
 
 
+# Per-source extra flags.  The forward keeps its MFMA accumulators in ordinary VGPRs: its score
+# tile is post-processed by VALU code every iteration and fits 2 waves per SIMD that way.
+FILE_FLAGS = {
+    "fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -39,7 +46,8 @@ def _hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), "-c", src, "-o", obj, *DEVICE_FLAGS]
+    cmd = [_hipcc(), "-c", src, "-o", obj, *DEVICE_FLAGS,
+           *FILE_FLAGS.get(os.path.basename(src), [])]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -33,6 +33,7 @@ namespace {
 constexpr int kBR = 128;   // query rows per workgroup
 constexpr int kBC = 64;    // keys per tile
 constexpr int kThreads = 256;
+constexpr float kSlack = 8.f;   // lazy-rescale threshold, log2 units (P <= 256)
 
 template <int D>
 struct FwdSmem {
@@ -53,13 +54,17 @@ struct TileRegs {
 template <int D>
 __device__ __forceinline__ void load_tile(TileRegs<D>& t, const bf16* __restrict__ K,
                                           const bf16* __restrict__ V, int k0, int Lk, int tid) {
+    // Rows at or beyond Lk are read from row Lk - 1 (always valid: a tile is only loaded when
+    // k0 < Lk) and replaced by zeros, so the loads need no branches.
     constexpr int C8 = D / 8;
+    const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < TileRegs<D>::KCH; ++i) {
         int id = tid + kThreads * i;
         int row = id / C8, col8 = id % C8;
         int key = k0 + row;
-        t.k[i] = key < Lk ? ld16(K + (size_t)key * D + col8 * 8) : u32x4{0, 0, 0, 0};
+        u32x4 x = ld16(K + (size_t)min(key, Lk - 1) * D + col8 * 8);
+        t.k[i] = key < Lk ? x : zero;
     }
     // V: thread -> (key group of 4, 8-column block); D = 64 leaves half the threads idle.
     int kg = tid & 15, col8 = tid >> 4;
@@ -67,7 +72,8 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& t, const bf16* __restrict
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             int key = k0 + 4 * kg + r;
-            t.v[r] = key < Lk ? ld16(V + (size_t)key * D + col8 * 8) : u32x4{0, 0, 0, 0};
+            u32x4 x = ld16(V + (size_t)min(key, Lk - 1) * D + col8 * 8);
+            t.v[r] = key < Lk ? x : zero;
         }
     }
 }
@@ -184,11 +190,19 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
-            mx = max_with_partner(mx);
-            const float mnew = fmaxf(m, mx * C);
-            const float muse = mnew == kNegInf ? 0.f : mnew;
-            const float alpha = exp2_hw(m - muse);
-            m = mnew;
+            mx = max_with_partner(mx) * C;
+            // Lazy rescaling: the reference point m only moves when some row of the wave sees a
+            // score more than kSlack (log2 units) above it; otherwise exponents stay <= 2^kSlack
+            // and O, l keep their scale.  Exact in real arithmetic: O and l share the same m.
+            if (__builtin_amdgcn_ballot_w64(mx > m + kSlack) != 0) {
+                const float mnew = fmaxf(m, mx);
+                const float alpha = mnew == kNegInf ? 1.f : exp2_hw(m - mnew);
+                m = mnew;
+                lsum *= alpha;
+#pragma unroll
+                for (int i = 0; i < ND; ++i) oacc[i] *= alpha;
+            }
+            const float muse = m == kNegInf ? 0.f : m;
             float rs = 0.f;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
@@ -198,9 +212,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
                     st[t][r] = e;
                     rs += e;
                 }
-            lsum = lsum * alpha + rs;
-#pragma unroll
-            for (int i = 0; i < ND; ++i) oacc[i] *= alpha;
+            lsum += rs;
 
             // P^T as B operands: (t, u) covers keys 32t + 16u + {8*(j/4) + 4*hh + j%4}.
             bf16x8 pf[2][2];
