@@ -57,9 +57,10 @@ def fwd_bytes_compulsory(B, Hq, Hkv, N, d, elem=2):
 
 
 def bwd_bytes_compulsory(B, Hq, Hkv, N, d, elem=2):
-    """Backward: read Q, K, V, O, dO (bf16), LSE; write+read D; write fp32 dQ, dK, dV."""
+    """Backward: read Q, K, V, O, dO (bf16), LSE; write+read the two per-row statistics; write
+    fp32 dQ, dK, dV."""
     reads = (3 * B * Hq * N * d + 2 * B * Hkv * N * d) * elem + B * Hq * N * 4
-    d_rw = 2 * B * Hq * N * 4
+    d_rw = 2 * 2 * B * Hq * N * 4
     writes = (B * Hq * N * d + 2 * B * Hkv * N * d) * 4
     return reads + d_rw + writes
 
@@ -200,8 +201,8 @@ def main():
             mark("fwd_bf16", lambda: fa.fa_fwd(q, k, v, scale=sc, causal=causal, key_lens=kl,
                                                o=o, lse=lse))
         if do_bwd:
-            mark("bwd_prep", lambda: fa.fa_bwd_prep(o, do, dq, ws))
-            mark("bwd_main", lambda: fa.fa_bwd_main(q, k, v, do, lse, dq, dk, dv, ws, scale=sc,
+            mark("bwd_prep", lambda: fa.fa_bwd_prep(o, do, lse, dq, ws))
+            mark("bwd_main", lambda: fa.fa_bwd_main(q, k, v, do, dq, dk, dv, ws, scale=sc,
                                                     causal=causal, key_lens=kl))
 
     for _ in range(args.warmup):

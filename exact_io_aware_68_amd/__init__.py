@@ -9,7 +9,8 @@ The functions carry the C names (see include/fa.h for the full contract):
 
     fa_fwd(q, k, v, *, scale, causal, key_lens, o, lse)              -> (o, lse)
     fa_bwd(q, k, v, o, dO, lse, *, scale, causal, key_lens, ...)     -> (dq, dk, dv)
-    fa_bwd_prep / fa_bwd_main                                        (the two stages of fa_bwd)
+    fa_bwd_prep(o, dO, lse, dq, workspace) / fa_bwd_main(q, k, v, dO, dq, dk, dv, workspace, ...)
+                                                                     (the two stages of fa_bwd)
     fa_bwd_workspace_size, fa_fwd_kernel_name, fa_bwd_kernel_name, fa_status_str, fa_abi_version
 
 Tensors are [B, H, N, d] contiguous ("BHND"); q/k/v/o/dO are bf16 (d in {64, 128}) or fp32
@@ -57,9 +58,9 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd.restype = I
     lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, Z, I, I, I, I, I, F, I, I, P]
     lib.fa_bwd.restype = I
-    lib.fa_bwd_prep.argtypes = [P, P, P, P, Z, I, I, I, I, I, P]
+    lib.fa_bwd_prep.argtypes = [P, P, P, P, P, Z, I, I, I, I, I, P]
     lib.fa_bwd_prep.restype = I
-    lib.fa_bwd_main.argtypes = [P, P, P, P, P, P, P, P, P, P, Z, I, I, I, I, I, F, I, I, P]
+    lib.fa_bwd_main.argtypes = [P, P, P, P, P, P, P, P, P, Z, I, I, I, I, I, F, I, I, P]
     lib.fa_bwd_main.restype = I
     lib.fa_bwd_workspace_size.argtypes = [I, I, I, I]
     lib.fa_bwd_workspace_size.restype = Z
@@ -160,18 +161,18 @@ def fa_fwd(q, k, v, *, scale: float | None = None, causal: bool = False, key_len
     return o, lse
 
 
-def fa_bwd_prep(o, dO, dq, workspace, *, stream=None):
+def fa_bwd_prep(o, dO, lse, dq, workspace, *, stream=None):
     B, Hq, N, d = o.shape
-    st = load().fa_bwd_prep(_ptr(o), _ptr(dO), _ptr(dq), _ptr(workspace),
+    st = load().fa_bwd_prep(_ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), B, Hq, N, d,
                             _dtype_code(o), _stream(stream, o.device))
     _check("fa_bwd_prep", st)
 
 
-def fa_bwd_main(q, k, v, dO, lse, dq, dk, dv, workspace, *, scale=None, causal=False,
+def fa_bwd_main(q, k, v, dO, dq, dk, dv, workspace, *, scale=None, causal=False,
                 key_lens=None, stream=None):
     B, Hq, Hkv, N, d = _shape(q, k)
-    st = load().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(key_lens),
+    st = load().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(key_lens),
                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), B, Hq, Hkv, N, d,
                             ctypes.c_float(_default_scale(d) if scale is None else scale),

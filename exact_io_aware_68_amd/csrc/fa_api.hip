@@ -102,7 +102,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 size_t fa_bwd_workspace_size(int B, int Hq, int N, int d) {
     if (B < 0 || Hq <= 0 || N < 0 || d <= 0) return 0;
-    return (size_t)B * (size_t)Hq * (size_t)N * sizeof(float);
+    return (size_t)B * (size_t)Hq * (size_t)N * 2 * sizeof(float);
 }
 
 static fa_status check_bwd_common(int B, int Hq, int Hkv, int N, int d, fa_dtype dtype,
@@ -118,27 +118,28 @@ static fa_status check_bwd_common(int B, int Hq, int Hkv, int N, int d, fa_dtype
     return FA_OK;
 }
 
-static fa_status validate_prep(const void* o, const void* dO, float* dq, const void* workspace,
-                               size_t workspace_bytes, int B, int Hq, int N, int d,
-                               fa_dtype dtype) {
+static fa_status validate_prep(const void* o, const void* dO, const float* lse, float* dq,
+                               const void* workspace, size_t workspace_bytes, int B, int Hq, int N,
+                               int d, fa_dtype dtype) {
     fa_status st = check_bwd_common(B, Hq, Hq, N, d, dtype, workspace_bytes, workspace);
     if (st != FA_OK || B == 0 || N == 0) return st;
-    if (!o || !dO || !dq) return FA_ERR_NULL;
-    if (misaligned(o, 16) || misaligned(dO, 16) || misaligned(dq, 16)) return FA_ERR_ALIGN;
+    if (!o || !dO || !lse || !dq) return FA_ERR_NULL;
+    if (misaligned(o, 16) || misaligned(dO, 16) || misaligned(dq, 16) || misaligned(lse, 4))
+        return FA_ERR_ALIGN;
     return FA_OK;
 }
 
 static fa_status validate_main(const void* q, const void* k, const void* v, const void* dO,
-                               const float* lse, const int32_t* key_lens, float* dq, float* dk,
-                               float* dv, const void* workspace, size_t workspace_bytes, int B,
-                               int Hq, int Hkv, int N, int d, float scale, fa_dtype dtype) {
+                               const int32_t* key_lens, float* dq, float* dk, float* dv,
+                               const void* workspace, size_t workspace_bytes, int B, int Hq,
+                               int Hkv, int N, int d, float scale, fa_dtype dtype) {
     fa_status st = check_bwd_common(B, Hq, Hkv, N, d, dtype, workspace_bytes, workspace);
     if (st != FA_OK) return st;
     if ((st = check_scale(scale)) != FA_OK) return st;
     if (B == 0 || N == 0) return FA_OK;
-    if (!q || !k || !v || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+    if (!q || !k || !v || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(dO, 16) ||
-        misaligned(lse, 4) || misaligned(key_lens, 4) || misaligned(dq, 16) ||
+        misaligned(key_lens, 4) || misaligned(dq, 16) ||
         misaligned(dk, 16) || misaligned(dv, 16))
         return FA_ERR_ALIGN;
     return FA_OK;
@@ -153,26 +154,26 @@ static fa::BwdParams bwd_params(const void* q, const void* k, const void* v, con
                          scale, causal ? 1 : 0};
 }
 
-fa_status fa_bwd_prep(const void* o, const void* dO, float* dq, void* workspace,
-                      size_t workspace_bytes, int B, int Hq, int N, int d, fa_dtype dtype,
-                      void* stream) {
-    fa_status st = validate_prep(o, dO, dq, workspace, workspace_bytes, B, Hq, N, d, dtype);
+fa_status fa_bwd_prep(const void* o, const void* dO, const float* lse, float* dq,
+                      void* workspace, size_t workspace_bytes, int B, int Hq, int N, int d,
+                      fa_dtype dtype, void* stream) {
+    fa_status st = validate_prep(o, dO, lse, dq, workspace, workspace_bytes, B, Hq, N, d, dtype);
     if (st != FA_OK || B == 0 || N == 0) return st;
     if ((st = device_ready()) != FA_OK) return st;
-    fa::BwdParams p = bwd_params(nullptr, nullptr, nullptr, o, dO, nullptr, nullptr, dq, nullptr,
+    fa::BwdParams p = bwd_params(nullptr, nullptr, nullptr, o, dO, lse, nullptr, dq, nullptr,
                                  nullptr, workspace, B, Hq, Hq, N, d, 1.f, 0);
     return launched(fa::launch_bwd_prep_bf16(p, static_cast<hipStream_t>(stream)));
 }
 
 fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dO,
-                      const float* lse, const int32_t* key_lens, float* dq, float* dk, float* dv,
+                      const int32_t* key_lens, float* dq, float* dk, float* dv,
                       const void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
                       int N, int d, float scale, int causal, fa_dtype dtype, void* stream) {
-    fa_status st = validate_main(q, k, v, dO, lse, key_lens, dq, dk, dv, workspace,
-                                 workspace_bytes, B, Hq, Hkv, N, d, scale, dtype);
+    fa_status st = validate_main(q, k, v, dO, key_lens, dq, dk, dv, workspace, workspace_bytes,
+                                 B, Hq, Hkv, N, d, scale, dtype);
     if (st != FA_OK || B == 0 || N == 0) return st;
     if ((st = device_ready()) != FA_OK) return st;
-    fa::BwdParams p = bwd_params(q, k, v, nullptr, dO, lse, key_lens, dq, dk, dv, workspace, B,
+    fa::BwdParams p = bwd_params(q, k, v, nullptr, dO, nullptr, key_lens, dq, dk, dv, workspace, B,
                                  Hq, Hkv, N, d, scale, causal);
     return launched(fa::launch_bwd_main_bf16(p, static_cast<hipStream_t>(stream)));
 }
@@ -182,10 +183,11 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
                  float scale, int causal, fa_dtype dtype, void* stream) {
     // Validate everything both stages need before launching either.
-    fa_status st = validate_main(q, k, v, dO, lse, key_lens, dq, dk, dv, workspace,
-                                 workspace_bytes, B, Hq, Hkv, N, d, scale, dtype);
+    fa_status st = validate_main(q, k, v, dO, key_lens, dq, dk, dv, workspace, workspace_bytes,
+                                 B, Hq, Hkv, N, d, scale, dtype);
     if (st != FA_OK || B == 0 || N == 0) return st;
-    if ((st = validate_prep(o, dO, dq, workspace, workspace_bytes, B, Hq, N, d, dtype)) != FA_OK)
+    if ((st = validate_prep(o, dO, lse, dq, workspace, workspace_bytes, B, Hq, N, d, dtype)) !=
+        FA_OK)
         return st;
     if ((st = device_ready()) != FA_OK) return st;
     fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, key_lens, dq, dk, dv, workspace, B, Hq,

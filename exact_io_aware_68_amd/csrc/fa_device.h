@@ -82,6 +82,32 @@ __device__ __forceinline__ void transpose4x8(const u32x4 r[4], u32x2 col[8]) {
     }
 }
 
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane 4a+b receives
+// element b of the 4-element (8-byte) chunks addressed by lanes a, a+4, a+8 and a+12 of the
+// group.  So if lane a+4e points at row r0+e, columns c0+4a..c0+4a+3 of a row-major bf16 matrix,
+// every lane receives one column (c0 + its index in the group) of four consecutive rows.
+__device__ __forceinline__ u32x2 lds_tr(const bf16* p) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+// Per-lane element offset for lds_tr_operand on a row-major matrix with row stride S: lane l
+// reads rows 4*(l/32) + (l%16)/4 (+8 for the second half) and columns 16*((l/16)%2) + 4*(l%4).
+__device__ __forceinline__ int tr_lane_offset(int lane, int S) {
+    const int G = lane >> 4, i = lane & 15;
+    return (4 * (G >> 1) + (i >> 2)) * S + 16 * (G & 1) + 4 * (i & 3);
+}
+
+// MFMA operand with the 8 reduction slots running down a column: lane l gets column
+// col0 + l%32 of rows r0 + 4*(l/32) + {0..3} (slots 0..3) and r0 + 8 + 4*(l/32) + {0..3}
+// (slots 4..7) — the same slot order as the C fragment rows 8*(r/4) + 4*(l/32) + r%4.
+// `base` = M + r0*S + col0 + tr_lane_offset(lane, S).
+__device__ __forceinline__ bf16x8 lds_tr_operand(const bf16* base, int S) {
+    return join(lds_tr(base), lds_tr(base + 8 * S));
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }

@@ -81,8 +81,9 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int causal, fa_dtype dtype, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs: one fp32 per query row (D_i = sum_c dO_ic O_ic),
- * i.e. B * Hq * N * 4 — linear in N, never N^2.  Returns 0 for an invalid shape.
+ * Bytes of device workspace fa_bwd needs: two fp32 per query row (D_i = sum_c dO_ic O_ic and
+ * the row's log-sum-exp in base 2), i.e. B * Hq * N * 8 — linear in N, never N^2.  Returns 0
+ * for an invalid shape.
  */
 size_t fa_bwd_workspace_size(int B, int Hq, int N, int d);
 
@@ -102,19 +103,20 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  float scale, int causal, fa_dtype dtype, void* stream);
 
 /*
- * First stage of fa_bwd: writes D_i = sum_c dO_ic O_ic (fp32) into the workspace and zeroes dq.
- * Same argument conventions as fa_bwd.
+ * First stage of fa_bwd: writes D_i = sum_c dO_ic O_ic and LSE_i * log2(e) (fp32) into the
+ * workspace and zeroes dq.  Same argument conventions as fa_bwd.
  */
-fa_status fa_bwd_prep(const void* o, const void* dO, float* dq, void* workspace,
-                      size_t workspace_bytes, int B, int Hq, int N, int d, fa_dtype dtype,
-                      void* stream);
+fa_status fa_bwd_prep(const void* o, const void* dO, const float* lse, float* dq,
+                      void* workspace, size_t workspace_bytes, int B, int Hq, int N, int d,
+                      fa_dtype dtype, void* stream);
 
 /*
  * Second stage of fa_bwd: recomputes S and P per tile and produces dq (accumulated into the
- * zeroed dq), dk and dv.  Requires fa_bwd_prep's workspace and zeroed dq, earlier on `stream`.
+ * zeroed dq), dk and dv.  Requires fa_bwd_prep's workspace and zeroed dq, earlier on `stream`
+ * (the row statistics, LSE included, are read from the workspace).
  */
 fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dO,
-                      const float* lse, const int32_t* key_lens, float* dq, float* dk, float* dv,
+                      const int32_t* key_lens, float* dq, float* dk, float* dv,
                       const void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
                       int N, int d, float scale, int causal, fa_dtype dtype, void* stream);
 

@@ -46,7 +46,7 @@ def test_status_strings(lib):
 
 
 def test_workspace_is_linear_in_N(lib):
-    assert fa.fa_bwd_workspace_size(2, 16, 4096, 128) == 2 * 16 * 4096 * 4
+    assert fa.fa_bwd_workspace_size(2, 16, 4096, 128) == 2 * 16 * 4096 * 8
     assert fa.fa_bwd_workspace_size(2, 16, 8192, 128) == 2 * fa.fa_bwd_workspace_size(2, 16, 4096, 128)
     assert fa.fa_bwd_workspace_size(-1, 16, 8, 64) == 0
 
@@ -94,7 +94,7 @@ def bwd(lib, q=A, k=A, v=A, o=A, do=A, lse=A, kl=None, dq=A, dk=A, dv=A, ws=A, w
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=fa.FA_F32), DTYPE), (dict(dtype=3), DTYPE), (dict(d=96), HEADDIM),
-    (dict(Hq=4, Hkv=3), GQA), (dict(ws=None), WORKSPACE), (dict(wsb=2 * 8 * 4 - 1), WORKSPACE),
+    (dict(Hq=4, Hkv=3), GQA), (dict(ws=None), WORKSPACE), (dict(wsb=2 * 8 * 8 - 1), WORKSPACE),
     (dict(scale=float("nan")), SCALE), (dict(do=None), NULL), (dict(lse=None), NULL),
     (dict(dq=A + 4), ALIGN), (dict(dk=A + 8), ALIGN), (dict(ws=A + 2), ALIGN),
     (dict(B=0, ws=None), OK),
