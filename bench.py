@@ -30,12 +30,19 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
-KERNEL_SRC = {                 # kernel -> source file whose hash guards stored counter data
-    "fwd_bf16": "exact_io_aware_68_amd/csrc/fa_fwd_bf16.hip",
-    "bwd_prep": "exact_io_aware_68_amd/csrc/fa_bwd_bf16.hip",
-    "bwd_main": "exact_io_aware_68_amd/csrc/fa_bwd_bf16.hip",
+_CSRC = "exact_io_aware_68_amd/csrc/"
+KERNEL_SRC = {                 # kernel -> sources whose hash guards stored counter data
+    "fwd_bf16": [_CSRC + "fa_fwd_bf16.hip", _CSRC + "fa_device.h"],
+    "bwd_prep": [_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_device.h"],
+    "bwd_main": [_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_device.h"],
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# rocprofv3 kernel-name fragment -> kernel key
+KERNEL_MATCH = [("bwd_prep", "bwd_prep"), ("bwd_main", "bwd_main"), ("fwd_bf16", "fwd_bf16")]
+COPY_CALIB_BYTES = 1 << 30
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
 
 
 # ------------------------------------------------------------------ work and byte models
@@ -80,21 +87,91 @@ def noreuse_tiled_bytes(B, Hq, N, d, Br=128, elem=2, causal=False):
 
 # ------------------------------------------------------------------ helpers
 
-def _src_hash(path):
-    return hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()[:16]
+def _src_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(kernel, workload):
-    """Measured HBM bytes per launch from committed rocprofv3 counter summaries, or None when
-    absent or taken on a different kernel source."""
+    """Measured HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) from the committed
+    rocprofv3 counter summary of this workload, or None when absent or when the kernel's sources
+    changed since the counters were taken."""
     try:
-        t = json.load(open(TRAFFIC_FILE))
-        e = t["kernels"][f"{kernel}@{workload}"]
-    except (OSError, KeyError, ValueError):
+        lines = open(traffic_file(workload)).read().splitlines()
+    except OSError:
         return None
-    if e.get("src_hash") != _src_hash(KERNEL_SRC[kernel]):
-        return None
-    return e["bytes_per_launch"]
+    for ln in lines:
+        cells = [c.strip() for c in ln.strip().strip("|").split("|")]
+        if len(cells) >= 6 and cells[0] == kernel:
+            if cells[1] != _src_hash(KERNEL_SRC[kernel]):
+                return None
+            try:
+                return int(cells[5])
+            except ValueError:
+                return None
+    return None
+
+
+def _counter_means(path):
+    """Mean Counter_Value per kernel key from a rocprofv3 counter_collection.csv."""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"]
+        key = next((k for frag, k in KERNEL_MATCH if frag in name), None)
+        if key is None and "copyBuffer" in name:
+            key = "copy"
+        if key is not None:
+            acc.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def traffic_summary(d, workload, cmd_note):
+    """Write profiles/hbm_traffic_<workload>.md from four rocprofv3 --pmc runs in directory d:
+    bench_FETCH_SIZE, bench_WRITE_SIZE (this bench) and copy_FETCH_SIZE, copy_WRITE_SIZE (the
+    --copy-calib copy of COPY_CALIB_BYTES).  Each counter (KiB per dispatch) is scaled by
+    known bytes / what the same counter reads for the copy."""
+    f = {n: _counter_means(os.path.join(d, f"{n}_counter_collection.csv"))
+         for n in ("bench_FETCH_SIZE", "bench_WRITE_SIZE", "copy_FETCH_SIZE", "copy_WRITE_SIZE")}
+    kib = COPY_CALIB_BYTES / 1024
+    fr = kib / f["copy_FETCH_SIZE"]["copy"]
+    fw = kib / f["copy_WRITE_SIZE"]["copy"]
+    import fa_inputs as fi
+    w = fi.WORKLOADS[workload]
+    comp = {"fwd_bf16": fwd_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d),
+            "bwd_prep": None, "bwd_main": None}
+    rows = []
+    for k in ("fwd_bf16", "bwd_prep", "bwd_main"):
+        if k not in f["bench_FETCH_SIZE"]:
+            continue
+        rd, wr = f["bench_FETCH_SIZE"][k], f["bench_WRITE_SIZE"][k]
+        byt = int(round((rd * fr + wr * fw) * 1024))
+        c = comp[k]
+        rows.append(f"| {k} | {_src_hash(KERNEL_SRC[k])} | {rd:.0f} | {wr:.0f} | "
+                    f"{(rd * fr + wr * fw) / 1024:.1f} | {byt} | "
+                    f"{'-' if c is None else f'{byt / c:.3f}'} |")
+    txt = f"""# HBM traffic per launch — workload {workload}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} \
+d={w.d} causal={w.causal} {w.dtype}
+
+Counters from four `rocprofv3 --pmc` runs (one counter each), averaged over the dispatches of
+each kernel:
+
+{cmd_note}
+
+Calibration: a plain device copy of {COPY_CALIB_BYTES} bytes (`bench.py --copy-calib`) reads
+FETCH_SIZE = {f['copy_FETCH_SIZE']['copy']:.0f} KiB and WRITE_SIZE =
+{f['copy_WRITE_SIZE']['copy']:.0f} KiB per dispatch, so FETCH_SIZE is scaled by {fr:.3f} and
+WRITE_SIZE by {fw:.3f}.  `bytes/launch` = calibrated FETCH + WRITE; `vs compulsory` divides by
+the tiled IO count (read Q, K, V once, write O and LSE once).  `src` is the hash bench.py
+compares with the kernel's current sources: a stale row reads as unmeasured.
+
+| kernel | src | FETCH_SIZE KiB | WRITE_SIZE KiB | calibrated MiB | bytes/launch | vs compulsory |
+|---|---|---|---|---|---|---|
+""" + "\n".join(rows) + "\n"
+    open(traffic_file(workload), "w").write(txt)
+    print(txt)
 
 
 def cpu_baseline(x, w, budget_s=20.0):
@@ -143,6 +220,15 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 
 # ------------------------------------------------------------------ main
 
+TRAFFIC_CMD = """    cd /tmp && export TMPDIR=/tmp
+    for C in FETCH_SIZE WRITE_SIZE; do
+      rocprofv3 --pmc $C -T -f csv -d $REPO/gpurun_out/pmc -o bench_$C -- \\
+          python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline
+      rocprofv3 --pmc $C -T -f csv -d $REPO/gpurun_out/pmc -o copy_$C -- \\
+          python3 $REPO/bench.py --copy-calib
+    done
+    python3 $REPO/bench.py --traffic-summary $REPO/gpurun_out/pmc"""
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,7 +238,12 @@ def main():
     ap.add_argument("--only", choices=["fwd", "bwd", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--traffic-summary", metavar="DIR",
+                    help="write profiles/hbm_traffic_<workload>.md from rocprofv3 --pmc CSVs")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary, args.workload, TRAFFIC_CMD)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the attention path is "
               "built and measured on a single MI355X", file=sys.stderr)
