@@ -108,6 +108,18 @@ __device__ __forceinline__ bf16x8 lds_tr_operand(const bf16* base, int S) {
     return join(lds_tr(base), lds_tr(base + 8 * S));
 }
 
+// Buffer resource over `bytes` bytes from `base` (raw addressing, 32-bit dword format).  Loads
+// through it at byte offsets >= bytes return zeros instead of touching memory, which the kernels
+// use for the tail rows of a tile: no clamped addresses and no selects.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }

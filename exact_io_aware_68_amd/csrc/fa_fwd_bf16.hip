@@ -51,30 +51,25 @@ struct TileRegs {
     u32x4 v[4];                                         // 4 key rows x 8 columns of V
 };
 
+// Issue the global loads of one K/V tile into registers.  The buffer resource covers only the
+// tile's valid rows (min(Lk - k0, kBC) of them), so rows at or beyond Lk come back as zeros
+// (NaN padding cannot leak through 0 * NaN in the P V product) and no address is clamped.  The
+// registers are consumed by store_tile at the end of the iteration, so the loads overlap it.
 template <int D>
 __device__ __forceinline__ void load_tile(TileRegs<D>& t, const bf16* __restrict__ K,
                                           const bf16* __restrict__ V, int k0, int Lk, int tid) {
-    // Rows at or beyond Lk are read from row Lk - 1 (always valid: a tile is only loaded when
-    // k0 < Lk) and replaced by zeros, so the loads need no branches.
     constexpr int C8 = D / 8;
-    const u32x4 zero = {0, 0, 0, 0};
+    const uint32_t bytes = (uint32_t)min(Lk - k0, kBC) * D * 2;
+    const rsrc_t rk = make_rsrc(K + (size_t)k0 * D, bytes);
+    const rsrc_t rv = make_rsrc(V + (size_t)k0 * D, bytes);
+    // K: chunk id = tid + kThreads * i covers row id / C8, columns 8 * (id % C8): byte id * 16.
 #pragma unroll
-    for (int i = 0; i < TileRegs<D>::KCH; ++i) {
-        int id = tid + kThreads * i;
-        int row = id / C8, col8 = id % C8;
-        int key = k0 + row;
-        u32x4 x = ld16(K + (size_t)min(key, Lk - 1) * D + col8 * 8);
-        t.k[i] = key < Lk ? x : zero;
-    }
+    for (int i = 0; i < TileRegs<D>::KCH; ++i) t.k[i] = buf_ld16(rk, (tid + kThreads * i) * 16);
     // V: thread -> (key group of 4, 8-column block); D = 64 leaves half the threads idle.
-    int kg = tid & 15, col8 = tid >> 4;
+    const int kg = tid & 15, col8 = tid >> 4;
     if (col8 < C8) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            int key = k0 + 4 * kg + r;
-            u32x4 x = ld16(V + (size_t)min(key, Lk - 1) * D + col8 * 8);
-            t.v[r] = key < Lk ? x : zero;
-        }
+        for (int r = 0; r < 4; ++r) t.v[r] = buf_ld16(rv, ((4 * kg + r) * D + col8 * 8) * 2);
     }
 }
 
