@@ -38,8 +38,9 @@ namespace fa {
 namespace {
 
 constexpr int kWaves = 4;       // waves per workgroup
-constexpr int kBC = 32;         // keys per tile
-constexpr int kNT = kBC / 32;   // 32-key blocks per tile
+constexpr int kBC = 32;         // keys per compute step
+constexpr int kNT = kBC / 32;   // 32-key blocks per compute step
+constexpr int kLT = 64;         // keys per LDS tile (two compute steps per barrier)
 constexpr int kThreads = 256;
 constexpr float kSlack = 8.f;   // lazy-rescale threshold, log2 units (P <= 256)
 
@@ -50,16 +51,16 @@ struct Flag {
 
 template <int D>
 struct FwdSmem {
-    static constexpr int KS = D + 16;       // K row stride (elements): 288 B rows for D = 128
-    static constexpr int VS = kBC + 8;      // V^T row stride (elements)
-    static constexpr int K_ELEMS = kBC * KS;
+    static constexpr int KS = D + 8;        // K row stride (elements): conflict-free row reads
+    static constexpr int VS = kLT + 8;      // V^T row stride (elements): conflict-free reads
+    static constexpr int K_ELEMS = kLT * KS;
     static constexpr int V_ELEMS = D * VS;
     static constexpr int TOTAL = 2 * K_ELEMS + 2 * V_ELEMS;
 };
 
 template <int D>
 struct KRegs {
-    static constexpr int N = kBC * D / 8 / kThreads;   // 16-byte K chunks per thread
+    static constexpr int N = kLT * D / 8 / kThreads;   // 16-byte K chunks per thread
     u32x4 k[N];
 };
 struct VRegs {
@@ -67,11 +68,11 @@ struct VRegs {
 };
 
 // Global -> register loads of one tile.  The buffer resource covers only the tile's valid rows
-// (min(Lk - k0, kBC)), so rows at or beyond Lk come back as zeros and no address is clamped.
+// (min(Lk - k0, kLT)), so rows at or beyond Lk come back as zeros and no address is clamped.
 template <int D>
 __device__ __forceinline__ void load_k(KRegs<D>& t, const bf16* __restrict__ K, int k0, int Lk,
                                        int tid) {
-    const rsrc_t r = make_rsrc(K + (size_t)k0 * D, (uint32_t)min(Lk - k0, kBC) * D * 2);
+    const rsrc_t r = make_rsrc(K + (size_t)k0 * D, (uint32_t)min(Lk - k0, kLT) * D * 2);
     // chunk id = tid + kThreads * i covers row id / (D/8), columns 8 * (id % (D/8)): byte id * 16
 #pragma unroll
     for (int i = 0; i < KRegs<D>::N; ++i) t.k[i] = buf_ld16(r, (tid + kThreads * i) * 16);
@@ -81,9 +82,9 @@ template <int D>
 __device__ __forceinline__ void load_v(VRegs& t, const bf16* __restrict__ V, int k0, int Lk,
                                        int tid) {
     constexpr int C8 = D / 8;
-    const rsrc_t r = make_rsrc(V + (size_t)k0 * D, (uint32_t)min(Lk - k0, kBC) * D * 2);
+    const rsrc_t r = make_rsrc(V + (size_t)k0 * D, (uint32_t)min(Lk - k0, kLT) * D * 2);
     // thread -> (group of 4 keys kg, 8-column block); threads beyond the tile stay idle
-    const int kg = tid % (kBC / 4), col8 = tid / (kBC / 4);
+    const int kg = tid % (kLT / 4), col8 = tid / (kLT / 4);
     if (col8 < C8) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) t.v[r4] = buf_ld16(r, ((4 * kg + r4) * D + col8 * 8) * 2);
@@ -101,6 +102,20 @@ __device__ __forceinline__ void store_k(const KRegs<D>& t, bf16* Ks, int tid) {
     }
 }
 
+// The two 32-row halves of a loaded K tile to separate destinations (nullptr: skip that half).
+template <int D>
+__device__ __forceinline__ void store_k_halves(const KRegs<D>& t, bf16* lo, bf16* hi, int tid) {
+    using S = FwdSmem<D>;
+    constexpr int C8 = D / 8;
+#pragma unroll
+    for (int i = 0; i < KRegs<D>::N; ++i) {
+        const int id = tid + kThreads * i;
+        const int row = id / C8;                 // rows < 32 exactly for i < N / 2
+        bf16* dst = i < KRegs<D>::N / 2 ? lo : hi;
+        if (dst) st16(dst + (row & 31) * S::KS + (id % C8) * 8, t.k[i]);
+    }
+}
+
 // V^T in LDS: row = head-dim column, positions = keys permuted within each group of 16 so that
 // position 16g + 8h + j holds key 16g + 8(j/4) + 4h + j%4 — the order of P^T's reduction slots
 // for lane half h.  The thread's 4-key group kg (keys 4kg..4kg+3) lands at position
@@ -109,7 +124,7 @@ template <int D>
 __device__ __forceinline__ void store_v(const VRegs& t, bf16* Vt, int tid) {
     using S = FwdSmem<D>;
     constexpr int C8 = D / 8;
-    const int kg = tid % (kBC / 4), col8 = tid / (kBC / 4);
+    const int kg = tid % (kLT / 4), col8 = tid / (kLT / 4);
     if (col8 < C8) {
         const int sub = kg & 3;
         const int pos = 16 * (kg >> 2) + 4 * (sub == 1 ? 2 : sub == 2 ? 1 : sub);
@@ -287,7 +302,19 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
                 }
     };
 
-    // ---- prologue: K(0), V(0), K(1) in LDS; S(0) and its max --------------------------------
+    // ---- prologue -----------------------------------------------------------------------------
+    // Compute step j covers keys 32j .. 32j + 31.  V^T LDS tile T holds keys 64T .. 64T + 63, so
+    // steps 2T and 2T+1 read its positions 0..31 and 32..63.  K LDS tile T is shifted by 32
+    // keys (keys 64T + 32 .. 64T + 95), so that the scores of steps 2T+1 and 2T+2 — computed in
+    // steps 2T and 2T+1 — read exactly one K tile; keys 0..31 sit in rows 32..63 of buffer 1.
+    // Tile T lives in buffer T % 2, and both K(T+1) and V(T+1) are loaded during steps 2T, 2T+1
+    // and stored after them, into the buffers of K(T-1) and V(T-1), released at the last barrier.
+    auto ksub = [&](int j) {   // K rows of step j
+        return Kb + (((j - 1) >> 1) & 1) * S::K_ELEMS + ((j - 1) & 1) * kBC * S::KS;
+    };
+    auto vsub = [&](int j) { return Vb + ((j >> 1) & 1) * S::V_ELEMS + (j & 1) * kBC; };
+    const int nlt = (kend + kLT - 1) / kLT;                       // V tiles
+    const int nkt = kend > kBC ? (kend - kBC + kLT - 1) / kLT : 0;  // shifted K tiles
     KRegs<D> kr;
     VRegs vr;
     f32x16 sa[NH][kNT], sb[NH][kNT];
@@ -295,63 +322,72 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
     if (ntiles > 0) {
         load_k<D>(kr, K, 0, Lk, tid);
         load_v<D>(vr, V, 0, Lk, tid);
-        store_k<D>(kr, Kb, tid);
+        store_k_halves<D>(kr, Kb + S::K_ELEMS + kBC * S::KS, Kb, tid);   // keys 0..31, 32..63
         store_v<D>(vr, Vb, tid);
-        if (ntiles > 1) {
-            load_k<D>(kr, K, kBC, Lk, tid);
-            store_k<D>(kr, Kb + S::K_ELEMS, tid);
+        if (kend > kLT) {
+            load_k<D>(kr, K, kLT, Lk, tid);
+            store_k_halves<D>(kr, Kb + kBC * S::KS, nullptr, tid);       // keys 64..95
         }
     }
     __syncthreads();
     if (ntiles > 0) {
-        scores(Kb, sa);
+        scores(ksub(0), sa);
         if (need_mask(0)) mask(0, sa);
         float alpha[NH];
         bool moved[NH];
         update_max(sa, alpha, moved);   // O is zero: no rescale needed
     }
+    __syncthreads();   // keys 0..31 in buffer 1 are overwritten by K tile 1 after steps 0, 1
+    // No global load is outstanding here; saying so keeps the wait analysis from carrying
+    // prologue loads into the loop, where it would wait for every new tile load at once.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
-    // ---- steady state: tile j with a successor ----------------------------------------------
+    // ---- steady state: step j with a successor ----------------------------------------------
     // cur holds S(j) (row max already folded into m); nxt receives S(j+1).  Between the loads at
     // the top and the rescale/stores at the bottom the step is one branch-free block, so the
-    // scheduler can interleave the MFMAs of S(j+1) and P(j) V(j) with the VALU work of tiles j
-    // and j+1.  MASKN says whether tile j+1 needs the causal / padding mask (compile time).
-    auto step = [&](auto maskn, int j, f32x16 (&cur)[NH][kNT], f32x16 (&nxt)[NH][kNT]) {
-        if (j + 2 < ntiles) load_k<D>(kr, K, (j + 2) * kBC, Lk, tid);
-        load_v<D>(vr, V, (j + 1) * kBC, Lk, tid);
-        scores(Kb + ((j + 1) & 1) * S::K_ELEMS, nxt);     // MFMA ...
+    // scheduler can interleave the MFMAs of S(j+1) and P(j) V(j) with the VALU work of steps j
+    // and j+1.  MASKN: step j+1 needs the causal / padding mask.  Even steps (j = 2T) issue the
+    // global loads of LDS tiles K(T+1) and V(T+1); odd steps store them and end with the barrier.
+    auto step = [&](auto maskn, auto odd, int j, f32x16 (&cur)[NH][kNT],
+                    f32x16 (&nxt)[NH][kNT]) {
+        const int T = j >> 1;
+        if constexpr (!decltype(odd)::value) {
+            if (T + 1 < nkt) load_k<D>(kr, K, (T + 1) * kLT + kBC, Lk, tid);
+            if (T + 1 < nlt) load_v<D>(vr, V, (T + 1) * kLT, Lk, tid);
+        }
+        scores(ksub(j + 1), nxt);                           // MFMA ...
         exponentiate(cur, pf);                              // ... alongside VALU
         if constexpr (decltype(maskn)::value) mask(j + 1, nxt);
-        pv(Vb + (j & 1) * S::V_ELEMS, pf);                  // MFMA ...
+        pv(vsub(j), pf);                                    // MFMA ...
         float alpha[NH];
         bool moved[NH];
         update_max(nxt, alpha, moved);                      // ... alongside VALU
         rescale(alpha, moved);
-        if (j + 2 < ntiles) store_k<D>(kr, Kb + (j & 1) * S::K_ELEMS, tid);
-        store_v<D>(vr, Vb + ((j + 1) & 1) * S::V_ELEMS, tid);
-        __syncthreads();
+        if constexpr (decltype(odd)::value) {
+            if (T + 1 < nkt) store_k<D>(kr, Kb + ((T + 1) & 1) * S::K_ELEMS, tid);
+            if (T + 1 < nlt) store_v<D>(vr, Vb + ((T + 1) & 1) * S::V_ELEMS, tid);
+            __syncthreads();
+        }
     };
-    // Tiles below jfree need no mask for any row of the workgroup.
+    // Steps below jfree need no mask for any row of the workgroup.
     int jfree = Lk / kBC;
     if (CAUSAL) jfree = min(jfree, (qt * kBR + 1) / kBC);
-    int j = 0;
+    int j = 0;   // stays even: pairs of steps share one LDS tile
     for (; j + 2 < ntiles && j + 2 < jfree; j += 2) {
-        step(Flag<false>{}, j, sa, sb);
-        step(Flag<false>{}, j + 1, sb, sa);
+        step(Flag<false>{}, Flag<false>{}, j, sa, sb);
+        step(Flag<false>{}, Flag<true>{}, j + 1, sb, sa);
     }
     for (; j + 2 < ntiles; j += 2) {
-        step(Flag<true>{}, j, sa, sb);
-        step(Flag<true>{}, j + 1, sb, sa);
+        step(Flag<true>{}, Flag<false>{}, j, sa, sb);
+        step(Flag<true>{}, Flag<true>{}, j + 1, sb, sa);
     }
     if (j + 1 < ntiles) {
-        step(Flag<true>{}, j, sa, sb);
-        ++j;
-        // last tile in sb
+        step(Flag<true>{}, Flag<false>{}, j, sa, sb);   // no loads left: nothing issued
         exponentiate(sb, pf);
-        pv(Vb + (j & 1) * S::V_ELEMS, pf);
+        pv(vsub(j + 1), pf);
     } else if (j < ntiles) {
         exponentiate(sa, pf);
-        pv(Vb + (j & 1) * S::V_ELEMS, pf);
+        pv(vsub(j), pf);
     }
 
     // ---- epilogue: O = Otilde / l (rounded to bf16), LSE = (m + log2 l) * ln 2 ---------------
