@@ -4,7 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu-baseline]
 
 One step = one pass of the whole hot path over one batch of synthetic inputs already resident
-in HBM: fa_fwd (O and LSE) then fa_bwd (its two stages, fa_bwd_prep and fa_bwd_main), bf16 with
+in HBM: fa_fwd (O and LSE) then fa_bwd (its stages fa_bwd_prep, fa_bwd_dkdv, fa_bwd_dq), bf16 with
 fp32 accumulation.  The default workload is causal attention at B=2, H=16, N=8192, d=128 — the
 shape the headline metric is quoted on — with Q, K, V, dO drawn N(0,1)*0.5 from seed 3.
 
@@ -34,10 +34,12 @@ _CSRC = "exact_io_aware_68_amd/csrc/"
 KERNEL_SRC = {                 # kernel -> sources whose hash guards stored counter data
     "fwd_bf16": [_CSRC + "fa_fwd_bf16.hip", _CSRC + "fa_device.h"],
     "bwd_prep": [_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_device.h"],
-    "bwd_main": [_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_device.h"],
+    "bwd_dkdv": [_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_device.h"],
+    "bwd_dq": [_CSRC + "fa_bwd_dq.hip", _CSRC + "fa_device.h"],
 }
 # rocprofv3 kernel-name fragment -> kernel key
-KERNEL_MATCH = [("bwd_prep", "bwd_prep"), ("bwd_main", "bwd_main"), ("fwd_bf16", "fwd_bf16")]
+KERNEL_MATCH = [("bwd_prep", "bwd_prep"), ("bwd_dkdv", "bwd_dkdv"), ("bwd_dq", "bwd_dq"),
+                ("fwd_bf16", "fwd_bf16")]
 COPY_CALIB_BYTES = 1 << 30
 
 
@@ -141,9 +143,9 @@ def traffic_summary(d, workload, cmd_note):
     import fa_inputs as fi
     w = fi.WORKLOADS[workload]
     comp = {"fwd_bf16": fwd_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d),
-            "bwd_prep": None, "bwd_main": None}
+            "bwd_prep": None, "bwd_dkdv": None, "bwd_dq": None}
     rows = []
-    for k in ("fwd_bf16", "bwd_prep", "bwd_main"):
+    for k in ("fwd_bf16", "bwd_prep", "bwd_dkdv", "bwd_dq"):
         if k not in f["bench_FETCH_SIZE"]:
             continue
         rd, wr = f["bench_FETCH_SIZE"][k], f["bench_WRITE_SIZE"][k]
@@ -275,7 +277,7 @@ def main():
     if do_bwd and not do_fwd:
         fa.fa_fwd(q, k, v, scale=sc, causal=causal, key_lens=kl, o=o, lse=lse)
 
-    names = (["fwd_bf16"] if do_fwd else []) + (["bwd_prep", "bwd_main"] if do_bwd else [])
+    names = (["fwd_bf16"] if do_fwd else []) + (["bwd_prep", "bwd_dkdv", "bwd_dq"] if do_bwd else [])
     ev = {n: [] for n in names}
 
     def step(record):
@@ -292,9 +294,11 @@ def main():
             mark("fwd_bf16", lambda: fa.fa_fwd(q, k, v, scale=sc, causal=causal, key_lens=kl,
                                                o=o, lse=lse))
         if do_bwd:
-            mark("bwd_prep", lambda: fa.fa_bwd_prep(o, do, lse, dq, ws))
-            mark("bwd_main", lambda: fa.fa_bwd_main(q, k, v, do, dq, dk, dv, ws, scale=sc,
+            mark("bwd_prep", lambda: fa.fa_bwd_prep(o, do, lse, ws))
+            mark("bwd_dkdv", lambda: fa.fa_bwd_dkdv(q, k, v, do, dk, dv, ws, scale=sc,
                                                     causal=causal, key_lens=kl))
+            mark("bwd_dq", lambda: fa.fa_bwd_dq(q, k, v, do, dq, ws, scale=sc, causal=causal,
+                                                key_lens=kl))
 
     for _ in range(args.warmup):
         step(False)
@@ -310,7 +314,14 @@ def main():
     ff = fwd_flops(w.B, w.Hq, w.N, w.d, causal) if do_fwd else 0.0
     bf = bwd_flops(w.B, w.Hq, w.N, w.d, causal) if do_bwd else 0.0
     value = (ff + bf) / (ms_step * 1e-3) / 1e12
-    flops_of = {"fwd_bf16": ff, "bwd_main": bf, "bwd_prep": 0.0}
+    # Per-kernel executed products (each the size of one forward product, ff / 2): dK/dV
+    # recomputes S and dP and forms dV, dK (4); dQ recomputes S and dP and forms dQ (3).  The
+    # step's value counts the method's 5 backward products only.
+    flops_of = {"fwd_bf16": ff, "bwd_prep": 0.0,
+                "bwd_dkdv": 2.0 * ff if do_bwd else 0.0, "bwd_dq": 1.5 * ff if do_bwd else 0.0}
+    if do_bwd and not do_fwd:
+        f1 = fwd_flops(w.B, w.Hq, w.N, w.d, causal)
+        flops_of.update(bwd_dkdv=2.0 * f1, bwd_dq=1.5 * f1)
     # dominant kernel: the one with the most time per step
     dom = max(names, key=lambda n: kern_ms[n])
     tr = stored_traffic(dom, args.workload)
@@ -345,11 +356,15 @@ def main():
             "noreuse_tiled_bytes": noreuse_tiled_bytes(w.B, w.Hq, w.N, w.d, causal=causal),
             "measured_bytes": stored_traffic("fwd_bf16", args.workload)},
         "bwd": None if not do_bwd else {
-            "tflops": round(bf / ((kern_ms["bwd_main"] + kern_ms["bwd_prep"]) * 1e-3) / 1e12, 2),
-            "main_tflops": round(bf / (kern_ms["bwd_main"] * 1e-3) / 1e12, 2),
-            "instance": fa.fa_bwd_kernel_name(w.d, causal, kl is not None, fa.FA_BF16),
+            "tflops": round(bf / (sum(kern_ms[n] for n in ("bwd_prep", "bwd_dkdv", "bwd_dq"))
+                                  * 1e-3) / 1e12, 2),
+            "dkdv_executed_tflops": round(flops_of["bwd_dkdv"] / (kern_ms["bwd_dkdv"] * 1e-3) / 1e12, 2),
+            "dq_executed_tflops": round(flops_of["bwd_dq"] / (kern_ms["bwd_dq"] * 1e-3) / 1e12, 2),
+            "instance": [fa.fa_bwd_dkdv_kernel_name(w.d, causal, kl is not None, fa.FA_BF16),
+                         fa.fa_bwd_dq_kernel_name(w.d, causal, kl is not None, fa.FA_BF16)],
             "compulsory_bytes": bwd_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d),
-            "measured_bytes": stored_traffic("bwd_main", args.workload)},
+            "measured_bytes": {n: stored_traffic(n, args.workload)
+                               for n in ("bwd_prep", "bwd_dkdv", "bwd_dq")}},
         "roofline": roof,
         "cpu_baseline": None,
     }

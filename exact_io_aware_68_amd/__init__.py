@@ -9,9 +9,10 @@ The functions carry the C names (see include/fa.h for the full contract):
 
     fa_fwd(q, k, v, *, scale, causal, key_lens, o, lse)              -> (o, lse)
     fa_bwd(q, k, v, o, dO, lse, *, scale, causal, key_lens, ...)     -> (dq, dk, dv)
-    fa_bwd_prep(o, dO, lse, dq, workspace) / fa_bwd_main(q, k, v, dO, dq, dk, dv, workspace, ...)
-                                                                     (the two stages of fa_bwd)
-    fa_bwd_workspace_size, fa_fwd_kernel_name, fa_bwd_kernel_name, fa_status_str, fa_abi_version
+    fa_bwd_prep(o, dO, lse, workspace), fa_bwd_dkdv(q, k, v, dO, dk, dv, workspace, ...),
+    fa_bwd_dq(q, k, v, dO, dq, workspace, ...)                       (the stages of fa_bwd)
+    fa_bwd_workspace_size, fa_fwd_kernel_name, fa_bwd_dkdv_kernel_name, fa_bwd_dq_kernel_name,
+    fa_status_str, fa_abi_version
 
 Tensors are [B, H, N, d] contiguous ("BHND"); q/k/v/o/dO are bf16 (d in {64, 128}) or fp32
 (forward only, d <= 128); lse is fp32 [B, Hq, N]; key_lens int32 [B] on the device; gradients
@@ -24,9 +25,9 @@ import math
 import os
 
 __all__ = [
-    "FAError", "lib_path", "load", "fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_main",
-    "fa_bwd_workspace_size", "fa_fwd_kernel_name", "fa_bwd_kernel_name", "fa_status_str",
-    "fa_abi_version", "FA_F32", "FA_BF16",
+    "FAError", "lib_path", "load", "fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq",
+    "fa_bwd_workspace_size", "fa_fwd_kernel_name", "fa_bwd_dkdv_kernel_name",
+    "fa_bwd_dq_kernel_name", "fa_status_str", "fa_abi_version", "FA_F32", "FA_BF16",
 ]
 
 FA_F32, FA_BF16 = 0, 1
@@ -58,13 +59,15 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd.restype = I
     lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, Z, I, I, I, I, I, F, I, I, P]
     lib.fa_bwd.restype = I
-    lib.fa_bwd_prep.argtypes = [P, P, P, P, P, Z, I, I, I, I, I, P]
+    lib.fa_bwd_prep.argtypes = [P, P, P, P, Z, I, I, I, I, I, P]
     lib.fa_bwd_prep.restype = I
-    lib.fa_bwd_main.argtypes = [P, P, P, P, P, P, P, P, P, Z, I, I, I, I, I, F, I, I, P]
-    lib.fa_bwd_main.restype = I
+    lib.fa_bwd_dkdv.argtypes = [P, P, P, P, P, P, P, P, Z, I, I, I, I, I, F, I, I, P]
+    lib.fa_bwd_dkdv.restype = I
+    lib.fa_bwd_dq.argtypes = [P, P, P, P, P, P, P, Z, I, I, I, I, I, F, I, I, P]
+    lib.fa_bwd_dq.restype = I
     lib.fa_bwd_workspace_size.argtypes = [I, I, I, I]
     lib.fa_bwd_workspace_size.restype = Z
-    for name in ("fa_fwd_kernel_name", "fa_bwd_kernel_name"):
+    for name in ("fa_fwd_kernel_name", "fa_bwd_dkdv_kernel_name", "fa_bwd_dq_kernel_name"):
         getattr(lib, name).argtypes = [I, I, I, I]
         getattr(lib, name).restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [I]
@@ -91,8 +94,12 @@ def fa_fwd_kernel_name(d: int, causal: bool, has_key_lens: bool, dtype: int) -> 
     return load().fa_fwd_kernel_name(d, int(causal), int(has_key_lens), dtype).decode()
 
 
-def fa_bwd_kernel_name(d: int, causal: bool, has_key_lens: bool, dtype: int) -> str:
-    return load().fa_bwd_kernel_name(d, int(causal), int(has_key_lens), dtype).decode()
+def fa_bwd_dkdv_kernel_name(d: int, causal: bool, has_key_lens: bool, dtype: int) -> str:
+    return load().fa_bwd_dkdv_kernel_name(d, int(causal), int(has_key_lens), dtype).decode()
+
+
+def fa_bwd_dq_kernel_name(d: int, causal: bool, has_key_lens: bool, dtype: int) -> str:
+    return load().fa_bwd_dq_kernel_name(d, int(causal), int(has_key_lens), dtype).decode()
 
 
 # ------------------------------------------------------------------ marshalling helpers
@@ -161,23 +168,33 @@ def fa_fwd(q, k, v, *, scale: float | None = None, causal: bool = False, key_len
     return o, lse
 
 
-def fa_bwd_prep(o, dO, lse, dq, workspace, *, stream=None):
+def fa_bwd_prep(o, dO, lse, workspace, *, stream=None):
     B, Hq, N, d = o.shape
-    st = load().fa_bwd_prep(_ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(workspace),
+    st = load().fa_bwd_prep(_ptr(o), _ptr(dO), _ptr(lse), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), B, Hq, N, d,
                             _dtype_code(o), _stream(stream, o.device))
     _check("fa_bwd_prep", st)
 
 
-def fa_bwd_main(q, k, v, dO, dq, dk, dv, workspace, *, scale=None, causal=False,
-                key_lens=None, stream=None):
+def fa_bwd_dkdv(q, k, v, dO, dk, dv, workspace, *, scale=None, causal=False, key_lens=None,
+                stream=None):
     B, Hq, Hkv, N, d = _shape(q, k)
-    st = load().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(key_lens),
-                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+    st = load().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(key_lens), _ptr(dk),
+                            _ptr(dv), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), B, Hq, Hkv, N, d,
                             ctypes.c_float(_default_scale(d) if scale is None else scale),
                             int(causal), _dtype_code(q), _stream(stream, q.device))
-    _check("fa_bwd_main", st)
+    _check("fa_bwd_dkdv", st)
+
+
+def fa_bwd_dq(q, k, v, dO, dq, workspace, *, scale=None, causal=False, key_lens=None,
+              stream=None):
+    B, Hq, Hkv, N, d = _shape(q, k)
+    st = load().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(key_lens), _ptr(dq),
+                          _ptr(workspace), workspace.numel() * workspace.element_size(), B, Hq,
+                          Hkv, N, d, ctypes.c_float(_default_scale(d) if scale is None else scale),
+                          int(causal), _dtype_code(q), _stream(stream, q.device))
+    _check("fa_bwd_dq", st)
 
 
 def fa_bwd(q, k, v, o, dO, lse, *, scale: float | None = None, causal: bool = False,

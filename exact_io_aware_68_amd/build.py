@@ -30,10 +30,12 @@ DEVICE_FLAGS = [
 ]
 
 
-# Per-source extra flags.  The forward keeps its MFMA accumulators in ordinary VGPRs: its score
-# tile is post-processed by VALU code every iteration and fits 2 waves per SIMD that way.
+# Per-source extra flags.  The forward and the dQ kernel keep their MFMA accumulators in ordinary
+# VGPRs: their score tiles are post-processed by VALU code every step and they fit 2 waves per
+# SIMD that way.
 FILE_FLAGS = {
     "fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fa_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

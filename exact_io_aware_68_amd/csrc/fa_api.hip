@@ -71,11 +71,19 @@ const char* fa_fwd_kernel_name(int d, int causal, int has_key_lens, fa_dtype dty
     return "none";
 }
 
-const char* fa_bwd_kernel_name(int d, int causal, int has_key_lens, fa_dtype dtype) {
+const char* fa_bwd_dkdv_kernel_name(int d, int causal, int has_key_lens, fa_dtype dtype) {
     (void)has_key_lens;
     if (dtype != FA_BF16) return "none";
-    if (d == 128) return causal ? "bwd_main_bf16<d128,causal>" : "bwd_main_bf16<d128>";
-    if (d == 64) return causal ? "bwd_main_bf16<d64,causal>" : "bwd_main_bf16<d64>";
+    if (d == 128) return causal ? "bwd_dkdv_bf16<d128,causal>" : "bwd_dkdv_bf16<d128>";
+    if (d == 64) return causal ? "bwd_dkdv_bf16<d64,causal>" : "bwd_dkdv_bf16<d64>";
+    return "none";
+}
+
+const char* fa_bwd_dq_kernel_name(int d, int causal, int has_key_lens, fa_dtype dtype) {
+    (void)has_key_lens;
+    if (dtype != FA_BF16) return "none";
+    if (d == 128) return causal ? "bwd_dq_bf16<d128,causal>" : "bwd_dq_bf16<d128>";
+    if (d == 64) return causal ? "bwd_dq_bf16<d64,causal>" : "bwd_dq_bf16<d64>";
     return "none";
 }
 
@@ -118,29 +126,28 @@ static fa_status check_bwd_common(int B, int Hq, int Hkv, int N, int d, fa_dtype
     return FA_OK;
 }
 
-static fa_status validate_prep(const void* o, const void* dO, const float* lse, float* dq,
+static fa_status validate_prep(const void* o, const void* dO, const float* lse,
                                const void* workspace, size_t workspace_bytes, int B, int Hq, int N,
                                int d, fa_dtype dtype) {
     fa_status st = check_bwd_common(B, Hq, Hq, N, d, dtype, workspace_bytes, workspace);
     if (st != FA_OK || B == 0 || N == 0) return st;
-    if (!o || !dO || !lse || !dq) return FA_ERR_NULL;
-    if (misaligned(o, 16) || misaligned(dO, 16) || misaligned(dq, 16) || misaligned(lse, 4))
-        return FA_ERR_ALIGN;
+    if (!o || !dO || !lse) return FA_ERR_NULL;
+    if (misaligned(o, 16) || misaligned(dO, 16) || misaligned(lse, 4)) return FA_ERR_ALIGN;
     return FA_OK;
 }
 
-static fa_status validate_main(const void* q, const void* k, const void* v, const void* dO,
-                               const int32_t* key_lens, float* dq, float* dk, float* dv,
+// Shared checks of the two gradient stages; `g0`, `g1` are their fp32 outputs (dk, dv or dq).
+static fa_status validate_grad(const void* q, const void* k, const void* v, const void* dO,
+                               const int32_t* key_lens, const float* g0, const float* g1,
                                const void* workspace, size_t workspace_bytes, int B, int Hq,
                                int Hkv, int N, int d, float scale, fa_dtype dtype) {
     fa_status st = check_bwd_common(B, Hq, Hkv, N, d, dtype, workspace_bytes, workspace);
     if (st != FA_OK) return st;
     if ((st = check_scale(scale)) != FA_OK) return st;
     if (B == 0 || N == 0) return FA_OK;
-    if (!q || !k || !v || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
+    if (!q || !k || !v || !dO || !g0 || !g1) return FA_ERR_NULL;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(dO, 16) ||
-        misaligned(key_lens, 4) || misaligned(dq, 16) ||
-        misaligned(dk, 16) || misaligned(dv, 16))
+        misaligned(key_lens, 4) || misaligned(g0, 16) || misaligned(g1, 16))
         return FA_ERR_ALIGN;
     return FA_OK;
 }
@@ -154,47 +161,63 @@ static fa::BwdParams bwd_params(const void* q, const void* k, const void* v, con
                          scale, causal ? 1 : 0};
 }
 
-fa_status fa_bwd_prep(const void* o, const void* dO, const float* lse, float* dq,
-                      void* workspace, size_t workspace_bytes, int B, int Hq, int N, int d,
-                      fa_dtype dtype, void* stream) {
-    fa_status st = validate_prep(o, dO, lse, dq, workspace, workspace_bytes, B, Hq, N, d, dtype);
+fa_status fa_bwd_prep(const void* o, const void* dO, const float* lse, void* workspace,
+                      size_t workspace_bytes, int B, int Hq, int N, int d, fa_dtype dtype,
+                      void* stream) {
+    fa_status st = validate_prep(o, dO, lse, workspace, workspace_bytes, B, Hq, N, d, dtype);
     if (st != FA_OK || B == 0 || N == 0) return st;
     if ((st = device_ready()) != FA_OK) return st;
-    fa::BwdParams p = bwd_params(nullptr, nullptr, nullptr, o, dO, lse, nullptr, dq, nullptr,
+    fa::BwdParams p = bwd_params(nullptr, nullptr, nullptr, o, dO, lse, nullptr, nullptr, nullptr,
                                  nullptr, workspace, B, Hq, Hq, N, d, 1.f, 0);
     return launched(fa::launch_bwd_prep_bf16(p, static_cast<hipStream_t>(stream)));
 }
 
-fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dO,
-                      const int32_t* key_lens, float* dq, float* dk, float* dv,
-                      const void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
-                      int N, int d, float scale, int causal, fa_dtype dtype, void* stream) {
-    fa_status st = validate_main(q, k, v, dO, key_lens, dq, dk, dv, workspace, workspace_bytes,
-                                 B, Hq, Hkv, N, d, scale, dtype);
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                      const int32_t* key_lens, float* dk, float* dv, const void* workspace,
+                      size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, float scale,
+                      int causal, fa_dtype dtype, void* stream) {
+    fa_status st = validate_grad(q, k, v, dO, key_lens, dk, dv, workspace, workspace_bytes, B,
+                                 Hq, Hkv, N, d, scale, dtype);
     if (st != FA_OK || B == 0 || N == 0) return st;
     if ((st = device_ready()) != FA_OK) return st;
-    fa::BwdParams p = bwd_params(q, k, v, nullptr, dO, nullptr, key_lens, dq, dk, dv, workspace, B,
-                                 Hq, Hkv, N, d, scale, causal);
-    return launched(fa::launch_bwd_main_bf16(p, static_cast<hipStream_t>(stream)));
+    fa::BwdParams p = bwd_params(q, k, v, nullptr, dO, nullptr, key_lens, nullptr, dk, dv,
+                                 workspace, B, Hq, Hkv, N, d, scale, causal);
+    return launched(fa::launch_bwd_dkdv_bf16(p, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+                    const int32_t* key_lens, float* dq, const void* workspace,
+                    size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, float scale,
+                    int causal, fa_dtype dtype, void* stream) {
+    fa_status st = validate_grad(q, k, v, dO, key_lens, dq, dq, workspace, workspace_bytes, B,
+                                 Hq, Hkv, N, d, scale, dtype);
+    if (st != FA_OK || B == 0 || N == 0) return st;
+    if ((st = device_ready()) != FA_OK) return st;
+    fa::BwdParams p = bwd_params(q, k, v, nullptr, dO, nullptr, key_lens, dq, nullptr, nullptr,
+                                 workspace, B, Hq, Hkv, N, d, scale, causal);
+    return launched(fa::launch_bwd_dq_bf16(p, static_cast<hipStream_t>(stream)));
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                  const float* lse, const int32_t* key_lens, float* dq, float* dk, float* dv,
                  void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
                  float scale, int causal, fa_dtype dtype, void* stream) {
-    // Validate everything both stages need before launching either.
-    fa_status st = validate_main(q, k, v, dO, key_lens, dq, dk, dv, workspace, workspace_bytes,
-                                 B, Hq, Hkv, N, d, scale, dtype);
+    // Validate everything the three stages need before launching any.
+    fa_status st = validate_grad(q, k, v, dO, key_lens, dk, dv, workspace, workspace_bytes, B,
+                                 Hq, Hkv, N, d, scale, dtype);
     if (st != FA_OK || B == 0 || N == 0) return st;
-    if ((st = validate_prep(o, dO, lse, dq, workspace, workspace_bytes, B, Hq, N, d, dtype)) !=
-        FA_OK)
+    if ((st = validate_grad(q, k, v, dO, key_lens, dq, dq, workspace, workspace_bytes, B, Hq, Hkv,
+                            N, d, scale, dtype)) != FA_OK)
+        return st;
+    if ((st = validate_prep(o, dO, lse, workspace, workspace_bytes, B, Hq, N, d, dtype)) != FA_OK)
         return st;
     if ((st = device_ready()) != FA_OK) return st;
     fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, key_lens, dq, dk, dv, workspace, B, Hq,
                                  Hkv, N, d, scale, causal);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = launched(fa::launch_bwd_prep_bf16(p, s))) != FA_OK) return st;
-    return launched(fa::launch_bwd_main_bf16(p, s));
+    if ((st = launched(fa::launch_bwd_dkdv_bf16(p, s))) != FA_OK) return st;
+    return launched(fa::launch_bwd_dq_bf16(p, s));
 }
 
 }  // extern "C"

@@ -120,6 +120,21 @@ __device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t voff) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
 
+// Global -> LDS copies through a buffer resource (no registers involved): lane i of the wave
+// writes bytes [n i, n i + n) of LDS from `lds` (wave-uniform), n = 16 or 4; bytes of the
+// resource at or beyond its size arrive as zeros.  Completion is tracked by the vector memory
+// counter: wait_vmem() before the barrier that publishes the data.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, const void* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                             (int)voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t voff, const void* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
+                                             (int)voff, 0, 0, 0);
+}
+// s_waitcnt vmcnt(0): every global load and LDS DMA of this wave has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }

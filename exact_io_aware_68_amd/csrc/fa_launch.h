@@ -30,7 +30,7 @@ struct BwdParams {
     float* dq;
     float* dk;
     float* dv;
-    float* Dsum;              // workspace: one fp32 per query row
+    float* Dsum;              // workspace: D per query row, then the base-2 LSE per row
     int B, Hq, Hkv, N, d;
     float scale;
     int causal;
@@ -39,6 +39,7 @@ struct BwdParams {
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_prep_bf16(const BwdParams& p, hipStream_t stream);
-hipError_t launch_bwd_main_bf16(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_dkdv_bf16(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_dq_bf16(const BwdParams& p, hipStream_t stream);
 
 }  // namespace fa

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum {
     FA_OK = 0,
@@ -93,9 +93,9 @@ size_t fa_bwd_workspace_size(int B, int Hq, int N, int d);
  * dk, dv [B][Hkv][N][d] — gradients of sum(O * dO) with respect to Q, K, V, where dK and dV of a
  * kv-head are summed over the q-heads of its group, and keys at or beyond key_lens[b] get zero.
  * workspace: device memory of at least fa_bwd_workspace_size() bytes, contents ignored.
- * Only FA_BF16 with d in {64, 128} is supported.  dq is accumulated with fp32 atomics, so its
- * low-order bits may vary from run to run; dk, dv and the forward are bitwise reproducible.
- * Equivalent to fa_bwd_prep followed by fa_bwd_main on the same stream.
+ * Only FA_BF16 with d in {64, 128} is supported.  Every output element is written exactly once
+ * (no atomics), so all three gradients are bitwise reproducible.
+ * Equivalent to fa_bwd_prep, then fa_bwd_dkdv and fa_bwd_dq, on the same stream.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                  const float* lse, const int32_t* key_lens, float* dq, float* dk, float* dv,
@@ -103,27 +103,37 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  float scale, int causal, fa_dtype dtype, void* stream);
 
 /*
- * First stage of fa_bwd: writes D_i = sum_c dO_ic O_ic and LSE_i * log2(e) (fp32) into the
- * workspace and zeroes dq.  Same argument conventions as fa_bwd.
+ * First stage of fa_bwd: writes D_i = sum_c dO_ic O_ic and LSE_i * log2(e) (fp32; +inf for a
+ * row with LSE = -inf) of every query row into the workspace.  Same argument conventions as
+ * fa_bwd.
  */
-fa_status fa_bwd_prep(const void* o, const void* dO, const float* lse, float* dq,
-                      void* workspace, size_t workspace_bytes, int B, int Hq, int N, int d,
-                      fa_dtype dtype, void* stream);
+fa_status fa_bwd_prep(const void* o, const void* dO, const float* lse, void* workspace,
+                      size_t workspace_bytes, int B, int Hq, int N, int d, fa_dtype dtype,
+                      void* stream);
 
 /*
- * Second stage of fa_bwd: recomputes S and P per tile and produces dq (accumulated into the
- * zeroed dq), dk and dv.  Requires fa_bwd_prep's workspace and zeroed dq, earlier on `stream`
- * (the row statistics, LSE included, are read from the workspace).
+ * dK and dV (fp32, overwritten), key-stationary: recomputes S and P per tile from q, k, v and
+ * the row statistics that fa_bwd_prep wrote into the workspace earlier on `stream`.
  */
-fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dO,
-                      const int32_t* key_lens, float* dq, float* dk, float* dv,
-                      const void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
-                      int N, int d, float scale, int causal, fa_dtype dtype, void* stream);
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                      const int32_t* key_lens, float* dk, float* dv, const void* workspace,
+                      size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, float scale,
+                      int causal, fa_dtype dtype, void* stream);
 
-/* Name of the kernel instance fa_fwd / fa_bwd_main would launch for these arguments
+/*
+ * dQ (fp32, overwritten), query-stationary: recomputes S, P and dP per tile; needs the same
+ * workspace as fa_bwd_dkdv.  The two are independent of each other.
+ */
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+                    const int32_t* key_lens, float* dq, const void* workspace,
+                    size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, float scale,
+                    int causal, fa_dtype dtype, void* stream);
+
+/* Name of the kernel instance fa_fwd / fa_bwd_dkdv / fa_bwd_dq would launch for these arguments
  * ("none" if unsupported); a static string, never freed. */
 const char* fa_fwd_kernel_name(int d, int causal, int has_key_lens, fa_dtype dtype);
-const char* fa_bwd_kernel_name(int d, int causal, int has_key_lens, fa_dtype dtype);
+const char* fa_bwd_dkdv_kernel_name(int d, int causal, int has_key_lens, fa_dtype dtype);
+const char* fa_bwd_dq_kernel_name(int d, int causal, int has_key_lens, fa_dtype dtype);
 
 /* Static description of a status code. */
 const char* fa_status_str(int status);

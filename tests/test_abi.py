@@ -28,8 +28,8 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_workspace_size",
-            "fa_status_str", "fa_abi_version"} <= set(names)
+    assert {"fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq",
+            "fa_bwd_workspace_size", "fa_status_str", "fa_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -56,8 +56,9 @@ def test_kernel_names(lib):
     assert fa.fa_fwd_kernel_name(64, False, True, fa.FA_BF16) == "fwd_bf16<d64>"
     assert fa.fa_fwd_kernel_name(96, False, False, fa.FA_BF16) == "none"
     assert fa.fa_fwd_kernel_name(64, False, False, fa.FA_F32) == "fwd_f32<dmax64>"
-    assert fa.fa_bwd_kernel_name(128, True, False, fa.FA_BF16) == "bwd_main_bf16<d128,causal>"
-    assert fa.fa_bwd_kernel_name(128, True, False, fa.FA_F32) == "none"
+    assert fa.fa_bwd_dkdv_kernel_name(128, True, False, fa.FA_BF16) == "bwd_dkdv_bf16<d128,causal>"
+    assert fa.fa_bwd_dq_kernel_name(64, False, False, fa.FA_BF16) == "bwd_dq_bf16<d64>"
+    assert fa.fa_bwd_dq_kernel_name(128, True, False, fa.FA_F32) == "none"
 
 
 def fwd(lib, q=A, k=A, v=A, o=A, lse=A, kl=None, B=1, Hq=2, Hkv=1, N=8, d=64, scale=0.125,
@@ -101,6 +102,28 @@ def bwd(lib, q=A, k=A, v=A, o=A, do=A, lse=A, kl=None, dq=A, dk=A, dv=A, ws=A, w
 ])
 def test_bwd_argument_errors_before_any_hip_call(lib, kw, code):
     assert bwd(lib, **kw) == code
+
+
+def test_bwd_stage_argument_errors(lib):
+    f = ctypes.c_float(0.1)
+    # fa_bwd_prep(o, dO, lse, ws, wsb, B, Hq, N, d, dtype, stream)
+    assert lib.fa_bwd_prep(A, A, None, A, 1 << 20, 1, 2, 8, 128, fa.FA_BF16, None) == NULL
+    assert lib.fa_bwd_prep(A, A, A, A, 8, 1, 2, 8, 128, fa.FA_BF16, None) == WORKSPACE
+    assert lib.fa_bwd_prep(A, A, A, A, 1 << 20, 1, 2, 8, 96, fa.FA_BF16, None) == HEADDIM
+    # fa_bwd_dkdv(q, k, v, dO, kl, dk, dv, ws, wsb, B, Hq, Hkv, N, d, scale, causal, dtype, s)
+    assert lib.fa_bwd_dkdv(A, A, A, A, None, None, A, A, 1 << 20, 1, 2, 1, 8, 128, f, 1,
+                           fa.FA_BF16, None) == NULL
+    assert lib.fa_bwd_dkdv(A, A, A, A, None, A, A + 4, A, 1 << 20, 1, 2, 1, 8, 128, f, 1,
+                           fa.FA_BF16, None) == ALIGN
+    assert lib.fa_bwd_dkdv(A, A, A, A, None, A, A, A, 1 << 20, 1, 3, 2, 8, 128, f, 1,
+                           fa.FA_BF16, None) == GQA
+    # fa_bwd_dq(q, k, v, dO, kl, dq, ws, wsb, B, Hq, Hkv, N, d, scale, causal, dtype, s)
+    assert lib.fa_bwd_dq(A, A, A, A, None, None, A, 1 << 20, 1, 2, 1, 8, 128, f, 1,
+                         fa.FA_BF16, None) == NULL
+    assert lib.fa_bwd_dq(A, A, A, A, None, A, None, 1 << 20, 1, 2, 1, 8, 128, f, 1,
+                         fa.FA_BF16, None) == WORKSPACE
+    assert lib.fa_bwd_dq(A, A, A, A, None, A, A, 1 << 20, 1, 2, 1, 8, 128, ctypes.c_float(0.0),
+                         1, fa.FA_BF16, None) == SCALE
 
 
 def _gpu_present():
