@@ -228,14 +228,37 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
                 // S = Q K^T and dP = dO V^T; C row r -> query 32 q2 + 8(r/4) + 4hh + r%4, column -> key.
                 f32x16 sa[2] = {f32x16{}, f32x16{}};
                 f32x16 pa[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-                for (int s = 0; s < NS; ++s)
+                // Operands of reduction step s+1 are read while the MFMAs of step s run; the
+                // fence per step keeps the scheduler from sinking each read next to its MFMA
+                // (which serialises one LDS round trip per MFMA).
+                bf16x8 cq[2], co[2];
+                auto rd = [&](int s, bf16x8 (&aq)[2], bf16x8 (&ao)[2]) {
 #pragma unroll
                     for (int q2 = 0; q2 < 2; ++q2) {
                         const int ro = 32 * q2 * D + qro[s];
-                        sa[q2] = mfma32(__builtin_bit_cast(bf16x8, ld16(Qc + ro)), kf[s], sa[q2]);
-                        pa[q2] = mfma32(__builtin_bit_cast(bf16x8, ld16(Oc + ro)), vf[s], pa[q2]);
+                        aq[q2] = __builtin_bit_cast(bf16x8, ld16(Qc + ro));
+                        ao[q2] = __builtin_bit_cast(bf16x8, ld16(Oc + ro));
                     }
+                };
+                rd(0, cq, co);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    bf16x8 nq[2], no[2];
+                    if (s + 1 < NS) rd(s + 1, nq, no);
+#pragma unroll
+                    for (int q2 = 0; q2 < 2; ++q2) {
+                        sa[q2] = mfma32(cq[q2], kf[s], sa[q2]);
+                        pa[q2] = mfma32(co[q2], vf[s], pa[q2]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (s + 1 < NS) {
+#pragma unroll
+                        for (int q2 = 0; q2 < 2; ++q2) {
+                            cq[q2] = nq[q2];
+                            co[q2] = no[q2];
+                        }
+                    }
+                }
                 // Phase fences keep the scheduler from hoisting the next phase's LDS reads
                 // across this one, which would push the live registers past the VGPR file.
                 __builtin_amdgcn_sched_barrier(0);
@@ -271,14 +294,27 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 // dV^T += dO^T P, dK^T += Q^T (scale dS): A = one d-column over 8 query rows.
+                // Same read-ahead as above, one (dt, u) pair of products at a time.
+                bf16x8 ao, aq;
+                auto rdt = [&](int g, bf16x8& o_, bf16x8& q_) {
+                    const int dt = g / 4, ru = 16 * (g % 4) * D;
+                    o_ = trop(Oc + ru, tro[dt][0], tro[dt][1]);
+                    q_ = trop(Qc + ru, tro[dt][0], tro[dt][1]);
+                };
+                rdt(0, ao, aq);
 #pragma unroll
-                for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int ru = 16 * u * D;
-                        dva[dt] = mfma32(trop(Oc + ru, tro[dt][0], tro[dt][1]), pf[u], dva[dt]);
-                        dka[dt] = mfma32(trop(Qc + ru, tro[dt][0], tro[dt][1]), sf[u], dka[dt]);
+                for (int g = 0; g < 4 * ND; ++g) {
+                    bf16x8 no, nq;
+                    if (g + 1 < 4 * ND) rdt(g + 1, no, nq);
+                    const int dt = g / 4, u = g % 4;
+                    dva[dt] = mfma32(ao, pf[u], dva[dt]);
+                    dka[dt] = mfma32(aq, sf[u], dka[dt]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (g + 1 < 4 * ND) {
+                        ao = no;
+                        aq = nq;
                     }
+                }
             }
             wait_vmem();       // this wave's share of tile it+1 has landed
             __syncthreads();   // tile it+1 visible; buffer `cur` of Q / dO free
