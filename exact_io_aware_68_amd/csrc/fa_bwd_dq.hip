@@ -51,7 +51,8 @@ template <int D>
 __device__ __forceinline__ void load_tile(TileRegs& t, const bf16* __restrict__ K,
                                           const bf16* __restrict__ V, int k0, int Lk, int tid) {
     constexpr int C8 = D / 8;
-    const int half = tid >> 7, i = tid & 127;
+    // which half a wave belongs to is uniform across it: keep the resource in scalar registers
+    const int half = __builtin_amdgcn_readfirstlane(tid >> 7), i = tid & 127;
     const int kg = i % (kBC / 4), col8 = i / (kBC / 4);
     if (col8 < C8) {
         const rsrc_t r = make_rsrc((half ? V : K) + (size_t)k0 * D,
@@ -166,12 +167,27 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
         if (j + 1 < ntiles) load_tile<D>(tr, K, V, k0 + kBC, Lk, tid);
 
         // S^T = K Q^T, dP^T = V dO^T: rows = the tile's 32 keys, columns = the wave's queries.
+        // Operands of reduction step s+1 are read while the MFMAs of step s run (one fence per
+        // step keeps each read from sinking next to its MFMA).
         f32x16 st = f32x16{}, pt = f32x16{};
+        bf16x8 ck, cv;
+        auto rd = [&](int s, bf16x8& k_, bf16x8& v_) {
+            const int ro = c * S::KS + 16 * s + 8 * hh;
+            k_ = __builtin_bit_cast(bf16x8, ld16(Ks + ro));
+            v_ = __builtin_bit_cast(bf16x8, ld16(Vs + ro));
+        };
+        rd(0, ck, cv);
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            const int ro = c * S::KS + 16 * s + 8 * hh;
-            st = mfma32(__builtin_bit_cast(bf16x8, ld16(Ks + ro)), qf[s], st);
-            pt = mfma32(__builtin_bit_cast(bf16x8, ld16(Vs + ro)), of[s], pt);
+            bf16x8 nk, nv;
+            if (s + 1 < NS) rd(s + 1, nk, nv);
+            st = mfma32(ck, qf[s], st);
+            pt = mfma32(cv, of[s], pt);
+            __builtin_amdgcn_sched_barrier(0);
+            if (s + 1 < NS) {
+                ck = nk;
+                cv = nv;
+            }
         }
         // P and dS (scale applied once at the end); C row r -> key k0 + 8(r/4) + 4hh + r%4.
         const bool need_mask = (CAUSAL && k0 + kBC - 1 > q0) || (k0 + kBC > Lk);
@@ -191,14 +207,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
             sf[u] = to_bf16x8(pt[8 * u], pt[8 * u + 1], pt[8 * u + 2], pt[8 * u + 3], pt[8 * u + 4],
                               pt[8 * u + 5], pt[8 * u + 6], pt[8 * u + 7]);
         // dQ^T += K^T dS^T; A operand = K^T rows (d = 32 dt + c) in the same key order.
+        auto rdk = [&](int g) {
+            return __builtin_bit_cast(
+                bf16x8, ld16(Kt + (32 * (g >> 1) + c) * S::TS + 16 * (g & 1) + 8 * hh));
+        };
+        bf16x8 kc = rdk(0);
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const bf16x8 kt = __builtin_bit_cast(
-                    bf16x8, ld16(Kt + (32 * dt + c) * S::TS + 16 * u + 8 * hh));
-                acc[dt] = mfma32(kt, sf[u], acc[dt]);
-            }
+        for (int g = 0; g < 2 * ND; ++g) {
+            bf16x8 kn;
+            if (g + 1 < 2 * ND) kn = rdk(g + 1);
+            acc[g >> 1] = mfma32(kc, sf[g & 1], acc[g >> 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (g + 1 < 2 * ND) kc = kn;
+        }
         if (j + 1 < ntiles) store_tile<D>(tr, smem + ((j + 1) & 1) * S::STAGE, tid);
         __syncthreads();
     }
