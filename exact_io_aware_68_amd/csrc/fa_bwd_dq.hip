@@ -41,24 +41,33 @@ struct DqSmem {
     static constexpr int STAGE = 2 * KV + KT;
 };
 
-// Threads 0..127 stage K (4 keys x 8 columns each), threads 128..255 stage V (D = 128; for D = 64
-// half of each group is idle).  Rows at or beyond Lk read as zeros through the buffer bound.
+// Staging registers of one tile.  The row-major K and V copies use the contiguous mapping
+// (chunk id = tid + 256 i covers row id / (D/8), columns 8 (id % (D/8))), whose LDS stores are
+// free of bank conflicts; the transposed K copy needs 4 keys x 8 columns per thread and is
+// loaded a second time in that shape by threads 0..127 (64 of them for D = 64).
+template <int D>
 struct TileRegs {
-    u32x4 r[4];
+    static constexpr int NR = kBC * D / 8 / kThreads;   // 16-byte chunks per thread, per matrix
+    u32x4 k[NR], v[NR];
+    u32x4 t[4];                                          // 4 keys x 8 columns of K
 };
 
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs& t, const bf16* __restrict__ K,
+__device__ __forceinline__ void load_tile(TileRegs<D>& t, const bf16* __restrict__ K,
                                           const bf16* __restrict__ V, int k0, int Lk, int tid) {
     constexpr int C8 = D / 8;
-    // which half a wave belongs to is uniform across it: keep the resource in scalar registers
-    const int half = __builtin_amdgcn_readfirstlane(tid >> 7), i = tid & 127;
-    const int kg = i % (kBC / 4), col8 = i / (kBC / 4);
-    if (col8 < C8) {
-        const rsrc_t r = make_rsrc((half ? V : K) + (size_t)k0 * D,
-                                   (uint32_t)min(Lk - k0, kBC) * D * 2);
+    const uint32_t nb = (uint32_t)min(Lk - k0, kBC) * D * 2;
+    const rsrc_t rk = make_rsrc(K + (size_t)k0 * D, nb);
+    const rsrc_t rv = make_rsrc(V + (size_t)k0 * D, nb);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) t.r[x] = buf_ld16(r, ((4 * kg + x) * D + col8 * 8) * 2);
+    for (int i = 0; i < TileRegs<D>::NR; ++i) {
+        t.k[i] = buf_ld16(rk, (tid + kThreads * i) * 16);
+        t.v[i] = buf_ld16(rv, (tid + kThreads * i) * 16);
+    }
+    const int kg = tid % (kBC / 4), col8 = tid / (kBC / 4);
+    if (col8 < C8) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) t.t[x] = buf_ld16(rk, ((4 * kg + x) * D + col8 * 8) * 2);
     }
 }
 
@@ -66,24 +75,24 @@ __device__ __forceinline__ void load_tile(TileRegs& t, const bf16* __restrict__ 
 // of 4 placed at position 16 (kg/4) + 4 swap(kg%4), swap exchanging 1 and 2: position
 // 16g + 8h + j then holds key 16g + 8(j/4) + 4h + j%4, the C fragment's key order.
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs& t, bf16* stage, int tid) {
+__device__ __forceinline__ void store_tile(const TileRegs<D>& t, bf16* stage, int tid) {
     using S = DqSmem<D>;
     constexpr int C8 = D / 8;
-    const int half = tid >> 7, i = tid & 127;
-    const int kg = i % (kBC / 4), col8 = i / (kBC / 4);
+#pragma unroll
+    for (int i = 0; i < TileRegs<D>::NR; ++i) {
+        const int id = tid + kThreads * i;
+        st16(stage + (id / C8) * S::KS + (id % C8) * 8, t.k[i]);
+        st16(stage + S::KV + (id / C8) * S::KS + (id % C8) * 8, t.v[i]);
+    }
+    const int kg = tid % (kBC / 4), col8 = tid / (kBC / 4);
     if (col8 < C8) {
-        bf16* rows = stage + half * S::KV;
+        bf16* Kt = stage + 2 * S::KV;
+        const int sub = kg & 3;
+        const int pos = 16 * (kg >> 2) + 4 * (sub == 1 ? 2 : sub == 2 ? 1 : sub);
+        u32x2 col[8];
+        transpose4x8(t.t, col);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) st16(rows + (4 * kg + x) * S::KS + col8 * 8, t.r[x]);
-        if (half == 0) {
-            bf16* Kt = stage + 2 * S::KV;
-            const int sub = kg & 3;
-            const int pos = 16 * (kg >> 2) + 4 * (sub == 1 ? 2 : sub == 2 ? 1 : sub);
-            u32x2 col[8];
-            transpose4x8(t.r, col);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) st8(Kt + (col8 * 8 + e) * S::TS + pos, col[e]);
-        }
+        for (int e = 0; e < 8; ++e) st8(Kt + (col8 * 8 + e) * S::TS + pos, col[e]);
     }
 }
 
@@ -150,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < ND; ++i) acc[i] = f32x16{};
 
-    TileRegs tr;
+    TileRegs<D> tr;
     if (ntiles > 0) {
         load_tile<D>(tr, K, V, 0, Lk, tid);
         store_tile<D>(tr, smem, tid);
