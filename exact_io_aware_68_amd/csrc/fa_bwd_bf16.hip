@@ -68,47 +68,6 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const bf16* __restri
     }
 }
 
-// Tiles in LDS are row-major with their 16-byte chunks XOR-swizzled per row, so that they can
-// be filled by DMA (one contiguous 1 KB block per wave instruction: no padding possible) and
-// still read without bank conflicts both ways they are read: 16 consecutive rows at one chunk
-// (MFMA operands along the head dimension) and the transpose reads (4 consecutive rows x 4
-// consecutive chunks).  Row r's chunk q sits at chunk q ^ swz(r).
-template <int W>   // row width in elements (64 or 128)
-__device__ __forceinline__ int swz(int r) {
-    if constexpr (W == 128) return 4 * (r & 3) + ((r >> 2) & 3);
-    else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-}
-template <int W>
-__device__ __forceinline__ int swz_at(int r, int col) {
-    return r * W + 8 * ((col >> 3) ^ swz<W>(r)) + (col & 7);
-}
-
-// DMA rows [0, R) of a row-major W-wide bf16 matrix (row 0 at g; rows >= nv read as zeros) into
-// a swizzled LDS tile; the 4 waves share the 1 KB blocks.
-template <int W, int R>
-__device__ __forceinline__ void dma_tile(const bf16* g, int nv, bf16* tile, int w, int lane) {
-    constexpr int CPR = W / 8;                 // 16-byte chunks per row
-    constexpr int BLK = R * CPR / 64;          // 1 KB blocks
-    const rsrc_t rs = make_rsrc(g, (uint32_t)min(nv, R) * W * 2);
-#pragma unroll
-    for (int i = 0; i < BLK / (kThreads / 64); ++i) {
-        const int blk = w + (kThreads / 64) * i;
-        const int L = 64 * blk + lane;
-        const int row = L / CPR, q = (L % CPR) ^ swz<W>(L / CPR);
-        dma16(rs, (row * CPR + q) * 16, tile + 512 * blk);
-    }
-}
-
-// Per-lane element offset of a transpose read (see lds_tr) at rows r0 + {0..3} (+8 for sec = 1),
-// columns col0 .. col0 + 31 of a swizzled W-wide tile, for r0 a multiple of 16 (added by the
-// caller as r0 * W): the swizzle of those rows does not depend on r0.
-template <int W>
-__device__ __forceinline__ int tr_swz_offset(int lane, int col0, int sec) {
-    const int R = 4 * (lane >> 5) + ((lane & 15) >> 2) + 8 * sec;
-    const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    return swz_at<W>(R, col);
-}
-
 template <int D>
 struct BwdLds {
     static constexpr int QT = kBQ * D;           // elements of one Q (or dO) tile
@@ -190,8 +149,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
         auto stage = [&](int it, int st) {
             int i0;
             const size_t rb = rowbase(it, i0);
-            dma_tile<D, kBQ>((const bf16*)p.q + (rb + i0) * D, N - i0, sm.q[st], w, lane);
-            dma_tile<D, kBQ>((const bf16*)p.dO + (rb + i0) * D, N - i0, sm.o[st], w, lane);
+            dma_tile<D, kBQ, kThreads / 64>((const bf16*)p.q + (rb + i0) * D, N - i0, sm.q[st], w, lane);
+            dma_tile<D, kBQ, kThreads / 64>((const bf16*)p.dO + (rb + i0) * D, N - i0, sm.o[st], w, lane);
             const uint32_t nb = (uint32_t)min(N - i0, kBQ) * 4;
             if (w == 0) dma4(make_rsrc(L2 + rb + i0, nb), lane * 4, sm.l2[st]);
             if (w == 1) dma4(make_rsrc(p.Dsum + rb + i0, nb), lane * 4, sm.dd[st]);

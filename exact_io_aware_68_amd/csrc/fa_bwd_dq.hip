@@ -14,11 +14,12 @@
 // Mapping on CDNA4 (the forward's, with the softmax statistics already known):
 //   * 4 waves x 32 query rows.  S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16 put one
 //     query per lane (column c of the C fragment), so LSE2 and D are lane constants.
-//   * dS^T, rounded to bf16, is directly the B operand of dQ^T += K^T dS^T; the A operand K^T is a
-//     transposed copy of the key tile in LDS with keys permuted within each group of 16 to match
-//     the C fragment's key order, one 16-byte read per operand.
-//   * 32-key tiles double-buffered in LDS (K rows, V rows, K^T); the next tile's global loads
-//     are issued before the MFMAs of the current one and written to LDS after them.
+//   * dS^T, rounded to bf16, is directly the B operand of dQ^T += K^T dS^T; the A operand K^T is
+//     read from the row-major key tile with transpose reads (ds_read_b64_tr_b16), whose slot
+//     order is the C fragment's key order: no transposed copy of K is made.
+//   * 64-key K and V tiles are copied global -> LDS by DMA (no staging registers) into
+//     XOR-swizzled tiles, double-buffered: the next tile's copy is issued before the current
+//     tile's MFMAs; one barrier per 64 keys, two 32-key compute steps per tile.
 //   * Causal: key tiles above the diagonal are never loaded; only diagonal and tail tiles are
 //     masked; query tiles run longest first; XCD-aware workgroup order.
 #include "fa_device.h"
@@ -29,84 +30,30 @@ namespace fa {
 namespace {
 
 constexpr int kBR = 128;        // query rows per workgroup
-constexpr int kBC = 32;         // keys per tile
+constexpr int kBC = 32;         // keys per compute step
+constexpr int kLT = 64;         // keys per LDS tile
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 
 template <int D>
-struct DqSmem {
-    static constexpr int KS = D + 8;        // K / V row stride (elements): conflict-free reads
-    static constexpr int TS = kBC + 8;      // K^T row stride (elements)
-    static constexpr int KV = kBC * KS;     // one K or V tile
-    static constexpr int KT = D * TS;       // one K^T tile
-    static constexpr int STAGE = 2 * KV + KT;
+struct DqLds {
+    bf16 k[2][kLT * D];         // swizzled K tiles, double-buffered
+    bf16 v[2][kLT * D];         // swizzled V tiles
 };
-
-// Staging registers of one tile.  The row-major K and V copies use the contiguous mapping
-// (chunk id = tid + 256 i covers row id / (D/8), columns 8 (id % (D/8))), whose LDS stores are
-// free of bank conflicts; the transposed K copy needs 4 keys x 8 columns per thread and is
-// loaded a second time in that shape by threads 0..127 (64 of them for D = 64).
-template <int D>
-struct TileRegs {
-    static constexpr int NR = kBC * D / 8 / kThreads;   // 16-byte chunks per thread, per matrix
-    u32x4 k[NR], v[NR];
-    u32x4 t[4];                                          // 4 keys x 8 columns of K
-};
-
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& t, const bf16* __restrict__ K,
-                                          const bf16* __restrict__ V, int k0, int Lk, int tid) {
-    constexpr int C8 = D / 8;
-    const uint32_t nb = (uint32_t)min(Lk - k0, kBC) * D * 2;
-    const rsrc_t rk = make_rsrc(K + (size_t)k0 * D, nb);
-    const rsrc_t rv = make_rsrc(V + (size_t)k0 * D, nb);
-#pragma unroll
-    for (int i = 0; i < TileRegs<D>::NR; ++i) {
-        t.k[i] = buf_ld16(rk, (tid + kThreads * i) * 16);
-        t.v[i] = buf_ld16(rv, (tid + kThreads * i) * 16);
-    }
-    const int kg = tid % (kBC / 4), col8 = tid / (kBC / 4);
-    if (col8 < C8) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) t.t[x] = buf_ld16(rk, ((4 * kg + x) * D + col8 * 8) * 2);
-    }
-}
-
-// K and V rows row-major; K additionally transposed (row = head-dim column) with the key groups
-// of 4 placed at position 16 (kg/4) + 4 swap(kg%4), swap exchanging 1 and 2: position
-// 16g + 8h + j then holds key 16g + 8(j/4) + 4h + j%4, the C fragment's key order.
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& t, bf16* stage, int tid) {
-    using S = DqSmem<D>;
-    constexpr int C8 = D / 8;
-#pragma unroll
-    for (int i = 0; i < TileRegs<D>::NR; ++i) {
-        const int id = tid + kThreads * i;
-        st16(stage + (id / C8) * S::KS + (id % C8) * 8, t.k[i]);
-        st16(stage + S::KV + (id / C8) * S::KS + (id % C8) * 8, t.v[i]);
-    }
-    const int kg = tid % (kBC / 4), col8 = tid / (kBC / 4);
-    if (col8 < C8) {
-        bf16* Kt = stage + 2 * S::KV;
-        const int sub = kg & 3;
-        const int pos = 16 * (kg >> 2) + 4 * (sub == 1 ? 2 : sub == 2 ? 1 : sub);
-        u32x2 col[8];
-        transpose4x8(t.t, col);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st8(Kt + (col8 * 8 + e) * S::TS + pos, col[e]);
-    }
-}
 
 }  // namespace
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
-    using S = DqSmem<D>;
     constexpr int NS = D / 16;      // reduction steps over d
     constexpr int ND = D / 32;      // 32-column blocks of d
-    __shared__ __attribute__((aligned(16))) bf16 smem[2 * S::STAGE];
+    __shared__ __attribute__((aligned(1024))) DqLds<D> sm;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6, c = lane & 31, hh = lane >> 5;
+    // The wave index is uniform across the wave; saying so keeps the DMA addresses derived from
+    // it in scalar registers.
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
     const int N = p.N;
     const int nqt = (N + kBR - 1) / kBR;
     const int lin = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -153,37 +100,40 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
 
     int kend = Lk;
     if (CAUSAL) kend = min(kend, qt * kBR + kBR);
-    const int ntiles = (kend + kBC - 1) / kBC;
+    const int ntiles = (kend + kLT - 1) / kLT;
 
     f32x16 acc[ND];
 #pragma unroll
     for (int i = 0; i < ND; ++i) acc[i] = f32x16{};
 
-    TileRegs<D> tr;
-    if (ntiles > 0) {
-        load_tile<D>(tr, K, V, 0, Lk, tid);
-        store_tile<D>(tr, smem, tid);
-    }
-    __syncthreads();
-    wait_vmem();   // nothing outstanding: keeps the loop's tile loads from being waited early
+    // Stage LDS tile t (keys 64 t ..) into buffer st; keys at or beyond Lk arrive as zeros.
+    auto stage = [&](int t, int st) {
+        const int k0 = t * kLT;
+        dma_tile<D, kLT, kWaves>(K + (size_t)k0 * D, Lk - k0, sm.k[st], w, lane);
+        dma_tile<D, kLT, kWaves>(V + (size_t)k0 * D, Lk - k0, sm.v[st], w, lane);
+    };
+    // Per-lane LDS offsets (relative to a 32-key half tile; the swizzle has period 16 rows).
+    // Row reads of K / V: row c, chunk 2s + hh.
+    int kro[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kro[s] = swz_at<D>(c, 16 * s + 8 * hh);
+    // Transpose reads of K^T: columns 32 dt + c, keys 16u + the C fragment's order.
+    int tro[ND][2];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) tro[dt][x] = tr_swz_offset<D>(lane, 32 * dt, x);
 
-    for (int j = 0; j < ntiles; ++j) {
-        const bf16* stage = smem + (j & 1) * S::STAGE;
-        const bf16* Ks = stage;
-        const bf16* Vs = stage + S::KV;
-        const bf16* Kt = stage + 2 * S::KV;
-        const int k0 = j * kBC;
-        if (j + 1 < ntiles) load_tile<D>(tr, K, V, k0 + kBC, Lk, tid);
-
-        // S^T = K Q^T, dP^T = V dO^T: rows = the tile's 32 keys, columns = the wave's queries.
+    // One 32-key compute step on the half tile at Ks / Vs holding keys k0 ..
+    auto step = [&](const bf16* Ks, const bf16* Vs, int k0) {
+        // S^T = K Q^T, dP^T = V dO^T: rows = the 32 keys, columns = the wave's queries.
         // Operands of reduction step s+1 are read while the MFMAs of step s run (one fence per
         // step keeps each read from sinking next to its MFMA).
         f32x16 st = f32x16{}, pt = f32x16{};
         bf16x8 ck, cv;
         auto rd = [&](int s, bf16x8& k_, bf16x8& v_) {
-            const int ro = c * S::KS + 16 * s + 8 * hh;
-            k_ = __builtin_bit_cast(bf16x8, ld16(Ks + ro));
-            v_ = __builtin_bit_cast(bf16x8, ld16(Vs + ro));
+            k_ = __builtin_bit_cast(bf16x8, ld16(Ks + kro[s]));
+            v_ = __builtin_bit_cast(bf16x8, ld16(Vs + kro[s]));
         };
         rd(0, ck, cv);
 #pragma unroll
@@ -215,10 +165,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
         for (int u = 0; u < 2; ++u)
             sf[u] = to_bf16x8(pt[8 * u], pt[8 * u + 1], pt[8 * u + 2], pt[8 * u + 3], pt[8 * u + 4],
                               pt[8 * u + 5], pt[8 * u + 6], pt[8 * u + 7]);
-        // dQ^T += K^T dS^T; A operand = K^T rows (d = 32 dt + c) in the same key order.
+        __builtin_amdgcn_sched_barrier(0);
+        // dQ^T += K^T dS^T; A operand = K^T rows (d = 32 dt + c), keys 16u + slot order.
         auto rdk = [&](int g) {
-            return __builtin_bit_cast(
-                bf16x8, ld16(Kt + (32 * (g >> 1) + c) * S::TS + 16 * (g & 1) + 8 * hh));
+            const bf16* base = Ks + 16 * (g & 1) * D;
+            return join(lds_tr(base + tro[g >> 1][0]), lds_tr(base + tro[g >> 1][1]));
         };
         bf16x8 kc = rdk(0);
 #pragma unroll
@@ -229,8 +180,20 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
             __builtin_amdgcn_sched_barrier(0);
             if (g + 1 < 2 * ND) kc = kn;
         }
-        if (j + 1 < ntiles) store_tile<D>(tr, smem + ((j + 1) & 1) * S::STAGE, tid);
-        __syncthreads();
+    };
+
+    if (ntiles > 0) stage(0, 0);
+    wait_vmem();
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int cur = t & 1;
+        if (t + 1 < ntiles) stage(t + 1, cur ^ 1);   // that buffer was released at the last barrier
+        const int k0 = t * kLT;
+        step(sm.k[cur], sm.v[cur], k0);
+        if (k0 + kBC < kend) step(sm.k[cur] + kBC * D, sm.v[cur] + kBC * D, k0 + kBC);
+        wait_vmem();       // this wave's share of tile t+1 has landed
+        __syncthreads();   // tile t+1 visible; buffer cur free
     }
 
     // dQ = scale dQ^T^T: lane = query row, C rows = 4 consecutive d per group.

@@ -148,4 +148,46 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int nblk) {
     return (bid & 7) * (nblk >> 3) + (bid >> 3);
 }
 
+// Tiles in LDS are row-major with their 16-byte chunks XOR-swizzled per row, so that they can
+// be filled by DMA (one contiguous 1 KB block per wave instruction: no padding possible) and
+// still read without bank conflicts both ways they are read: 16 consecutive rows at one chunk
+// (MFMA operands along the head dimension) and the transpose reads (4 consecutive rows x 4
+// consecutive chunks).  Row r's chunk q sits at chunk q ^ swz(r).
+template <int W>   // row width in elements (64 or 128)
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (W == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+    else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+template <int W>
+__device__ __forceinline__ int swz_at(int r, int col) {
+    return r * W + 8 * ((col >> 3) ^ swz<W>(r)) + (col & 7);
+}
+
+// DMA rows [0, R) of a row-major W-wide bf16 matrix (row 0 at g; rows >= nv read as zeros) into
+// a swizzled LDS tile; the NW waves of the workgroup (w = this wave) share the 1 KB blocks.
+template <int W, int R, int NW>
+__device__ __forceinline__ void dma_tile(const bf16* g, int nv, bf16* tile, int w, int lane) {
+    constexpr int CPR = W / 8;                 // 16-byte chunks per row
+    constexpr int BLK = R * CPR / 64;          // 1 KB blocks
+    const rsrc_t rs = make_rsrc(g, (uint32_t)min(nv, R) * W * 2);
+    static_assert(BLK % NW == 0, "tile blocks must split evenly over the waves");
+#pragma unroll
+    for (int i = 0; i < BLK / NW; ++i) {
+        const int blk = w + NW * i;
+        const int L = 64 * blk + lane;
+        const int row = L / CPR, q = (L % CPR) ^ swz<W>(L / CPR);
+        dma16(rs, (row * CPR + q) * 16, tile + 512 * blk);
+    }
+}
+
+// Per-lane element offset of a transpose read (see lds_tr) at rows r0 + {0..3} (+8 for sec = 1),
+// columns col0 .. col0 + 31 of a swizzled W-wide tile, for r0 a multiple of 16 (added by the
+// caller as r0 * W): the swizzle of those rows does not depend on r0.
+template <int W>
+__device__ __forceinline__ int tr_swz_offset(int lane, int col0, int sec) {
+    const int R = 4 * (lane >> 5) + ((lane & 15) >> 2) + 8 * sec;
+    const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    return swz_at<W>(R, col);
+}
+
 }  // namespace fa
