@@ -169,7 +169,9 @@ template <int W, int R, int NW>
 __device__ __forceinline__ void dma_tile(const bf16* g, int nv, bf16* tile, int w, int lane) {
     constexpr int CPR = W / 8;                 // 16-byte chunks per row
     constexpr int BLK = R * CPR / 64;          // 1 KB blocks
-    const rsrc_t rs = make_rsrc(g, (uint32_t)min(nv, R) * W * 2);
+    // (clamped in scalar registers: a vector clamp would make the resource look divergent)
+    const int rows = __builtin_amdgcn_readfirstlane(max(min(nv, R), 0));
+    const rsrc_t rs = make_rsrc(g, (uint32_t)rows * W * 2);
     static_assert(BLK % NW == 0, "tile blocks must split evenly over the waves");
 #pragma unroll
     for (int i = 0; i < BLK / NW; ++i) {

@@ -2,34 +2,38 @@
 //
 // Method (guide page "FlashAttention", section "Tiling through SRAM"; tutorial page "Flash
 // attention and efficient attention", "Derivation: Incremental Softmax" and "Worked example"):
-// a workgroup keeps a tile of 256 query rows on chip, streams 64-key tiles of K and V through
+// a workgroup keeps a tile of 128 query rows on chip, streams 64-key tiles of K and V through
 // LDS, computes the score tile, folds it into the running max m, running sum l and the rescaled
-// unnormalised output (step 3 of the derivation, applied once per key tile), and writes only
+// unnormalised output (step 3 of the derivation, applied once per 32 keys), and writes only
 // O = Otilde / l and LSE = m + ln l.  The N x N score matrix never leaves registers.
 //
 // Mapping on CDNA4:
-//   * 4 waves x 64 query rows (two 32-row halves per wave), one wave per SIMD.  Every K and V
-//     fragment a wave reads from LDS feeds two MFMAs (one per half), which halves the LDS read
-//     traffic per flop compared with 32 rows per wave; at 32 rows the LDS reads alone would
-//     need about as many cycles as the MFMAs.
-//   * Each half computes the TRANSPOSED score tile S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so
-//     every lane owns one query row (column c of the C fragment) and 32 of the tile's 64 keys;
-//     its partner lane c+32 owns the other 32.  Row max and row sum are lane-local plus one
-//     v_permlane32_swap — no LDS round trip.
+//   * 4 waves x 32 query rows, two workgroups (8 waves) per CU.  Each wave computes the
+//     TRANSPOSED score tile S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so every lane owns one
+//     query row (column c of the C fragment) and 16 of the step's 32 keys; its partner lane c+32
+//     owns the other 16.  Row max and row sum are lane-local plus one v_permlane32_swap.
 //   * The C fragment of S^T, exponentiated and rounded to bf16, is directly the B operand of
-//     O^T += V^T P^T.  The V tile is stored transposed in LDS with its keys permuted within each
-//     group of 16 so that the A operand matching P^T's slot order is one 16-byte read.
-//   * Software pipeline per key tile j: the MFMAs of S(j+1) run while the VALU exponentiates
-//     tile j; the MFMAs of P(j) V(j) run while the VALU takes the row max of tile j+1.
+//     O^T += V^T P^T.  The A operand V^T comes from transpose reads (ds_read_b64_tr_b16) of the
+//     row-major V tile, whose slot order is the C fragment's key order: no transposed copy.
+//   * K and V tiles reach LDS by DMA (buffer_load ... lds: no staging registers, no LDS stores)
+//     into XOR-swizzled tiles that both the row reads of K and the transpose reads of V see
+//     without bank conflicts.  K tiles are shifted by 32 keys against V tiles, because the step
+//     that multiplies P(j) V(j) already computes S(j+1): one LDS tile pair then serves two
+//     32-key steps, one barrier per 64 keys.
+//   * Software pipeline per 32-key step j: the MFMAs of S(j+1) run while the VALU
+//     exponentiates step j; the MFMAs of P(j) V(j) run while the VALU takes the row max of
+//     S(j+1).  The interleaving itself is left to the compiler's scheduler, which measured
+//     faster than a hand-fenced order (one MFMA per fence, operands read one MFMA ahead).
+//   * The kernel is templated on NH, 32-row query halves per wave; the built instances use
+//     NH = 1 (two waves per SIMD): NH = 2 halves the LDS reads per flop but needs more
+//     registers than two waves per SIMD allow and measured slower at one wave per SIMD.
 //   * Scores are kept in log2 units: 2^(s * scale * log2 e - m) uses one FMA and v_exp_f32.
 //     The reference point m moves lazily (only when a score exceeds it by 2^8), which is exact
 //     in real arithmetic because Otilde and l always share the same reference point.
-//   * K/V tiles are double-buffered in LDS; the global loads of K(j+2) and V(j+1) are issued at
-//     the top of iteration j and written to LDS at its end (one barrier per tile).  They are
-//     buffer loads bounded to the tile's valid keys, so keys >= key_lens[b] read as zeros (NaN
-//     padding cannot leak through 0 * NaN in P V) and are masked to -inf before the max.
-//   * Causal: tiles entirely above the diagonal are never loaded; only diagonal and tail tiles
-//     are masked; q-tiles of a head run longest first; XCD-aware workgroup order.
+//   * Keys at or beyond key_lens[b] arrive as zeros (the DMA's buffer bound), so NaN padding
+//     cannot leak through 0 * NaN in P V, and are masked to -inf before the max.
+//   * Causal: tiles entirely above the diagonal are never loaded; only diagonal and tail steps
+//     are masked; query tiles of a head run longest first; XCD-aware workgroup order.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -50,90 +54,10 @@ struct Flag {
 };
 
 template <int D>
-struct FwdSmem {
-    static constexpr int KS = D + 8;        // K row stride (elements): conflict-free row reads
-    static constexpr int VS = kLT + 8;      // V^T row stride (elements): conflict-free reads
-    static constexpr int K_ELEMS = kLT * KS;
-    static constexpr int V_ELEMS = D * VS;
-    static constexpr int TOTAL = 2 * K_ELEMS + 2 * V_ELEMS;
+struct FwdLds {
+    bf16 k[2][kLT * D];   // swizzled K tiles (shifted by 32 keys), double-buffered
+    bf16 v[2][kLT * D];   // swizzled V tiles
 };
-
-template <int D>
-struct KRegs {
-    static constexpr int N = kLT * D / 8 / kThreads;   // 16-byte K chunks per thread
-    u32x4 k[N];
-};
-struct VRegs {
-    u32x4 v[4];                                        // 4 key rows x 8 columns of V
-};
-
-// Global -> register loads of one tile.  The buffer resource covers only the tile's valid rows
-// (min(Lk - k0, kLT)), so rows at or beyond Lk come back as zeros and no address is clamped.
-template <int D>
-__device__ __forceinline__ void load_k(KRegs<D>& t, const bf16* __restrict__ K, int k0, int Lk,
-                                       int tid) {
-    const rsrc_t r = make_rsrc(K + (size_t)k0 * D, (uint32_t)min(Lk - k0, kLT) * D * 2);
-    // chunk id = tid + kThreads * i covers row id / (D/8), columns 8 * (id % (D/8)): byte id * 16
-#pragma unroll
-    for (int i = 0; i < KRegs<D>::N; ++i) t.k[i] = buf_ld16(r, (tid + kThreads * i) * 16);
-}
-
-template <int D>
-__device__ __forceinline__ void load_v(VRegs& t, const bf16* __restrict__ V, int k0, int Lk,
-                                       int tid) {
-    constexpr int C8 = D / 8;
-    const rsrc_t r = make_rsrc(V + (size_t)k0 * D, (uint32_t)min(Lk - k0, kLT) * D * 2);
-    // thread -> (group of 4 keys kg, 8-column block); threads beyond the tile stay idle
-    const int kg = tid % (kLT / 4), col8 = tid / (kLT / 4);
-    if (col8 < C8) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) t.v[r4] = buf_ld16(r, ((4 * kg + r4) * D + col8 * 8) * 2);
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void store_k(const KRegs<D>& t, bf16* Ks, int tid) {
-    using S = FwdSmem<D>;
-    constexpr int C8 = D / 8;
-#pragma unroll
-    for (int i = 0; i < KRegs<D>::N; ++i) {
-        const int id = tid + kThreads * i;
-        st16(Ks + (id / C8) * S::KS + (id % C8) * 8, t.k[i]);
-    }
-}
-
-// The two 32-row halves of a loaded K tile to separate destinations (nullptr: skip that half).
-template <int D>
-__device__ __forceinline__ void store_k_halves(const KRegs<D>& t, bf16* lo, bf16* hi, int tid) {
-    using S = FwdSmem<D>;
-    constexpr int C8 = D / 8;
-#pragma unroll
-    for (int i = 0; i < KRegs<D>::N; ++i) {
-        const int id = tid + kThreads * i;
-        const int row = id / C8;                 // rows < 32 exactly for i < N / 2
-        bf16* dst = i < KRegs<D>::N / 2 ? lo : hi;
-        if (dst) st16(dst + (row & 31) * S::KS + (id % C8) * 8, t.k[i]);
-    }
-}
-
-// V^T in LDS: row = head-dim column, positions = keys permuted within each group of 16 so that
-// position 16g + 8h + j holds key 16g + 8(j/4) + 4h + j%4 — the order of P^T's reduction slots
-// for lane half h.  The thread's 4-key group kg (keys 4kg..4kg+3) lands at position
-// 16 (kg/4) + 4 swap(kg%4), where swap exchanges 1 and 2.
-template <int D>
-__device__ __forceinline__ void store_v(const VRegs& t, bf16* Vt, int tid) {
-    using S = FwdSmem<D>;
-    constexpr int C8 = D / 8;
-    const int kg = tid % (kLT / 4), col8 = tid / (kLT / 4);
-    if (col8 < C8) {
-        const int sub = kg & 3;
-        const int pos = 16 * (kg >> 2) + 4 * (sub == 1 ? 2 : sub == 2 ? 1 : sub);
-        u32x2 col[8];
-        transpose4x8(t.v, col);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st8(Vt + (col8 * 8 + e) * S::VS + pos, col[e]);
-    }
-}
 
 }  // namespace
 
@@ -144,17 +68,17 @@ constexpr int rows_per_block() { return kWaves * 32 * NH; }
 
 template <int D, bool CAUSAL, int NH>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
-    using S = FwdSmem<D>;
     constexpr int kBR = rows_per_block<NH>();
     constexpr int kWR = 32 * NH;
     constexpr int NS = D / 16;      // reduction steps of Q K^T
     constexpr int ND = D / 32;      // 32-column blocks of O
-    __shared__ __attribute__((aligned(16))) bf16 smem[S::TOTAL];
-    bf16* const Kb = smem;                       // K buffers 0, 1
-    bf16* const Vb = smem + 2 * S::K_ELEMS;      // V^T buffers 0, 1
+    __shared__ __attribute__((aligned(1024))) FwdLds<D> sm;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6, c = lane & 31, hh = lane >> 5;
+    // The wave index is uniform across the wave; saying so keeps the DMA addresses derived from
+    // it in scalar registers.
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
     const int nqt = (p.N + kBR - 1) / kBR;
     const int lin = xcd_logical_block(blockIdx.x, gridDim.x);
     const int head = lin / nqt;
@@ -203,7 +127,19 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
     }
 
     // ---- building blocks of one tile -------------------------------------------------------
-    // S^T for both halves from one K buffer: each K fragment feeds two MFMAs.
+    // S^T for all halves from one K fragment read.
+    // Per-lane LDS offsets within a 32-key half tile (the swizzle has period 16 rows).  Row
+    // reads of K: row c, chunk 2s + hh.
+    int kro[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kro[s] = swz_at<D>(c, 16 * s + 8 * hh);
+    // Transpose reads of V^T: columns 32 dt + c, keys 16u + the C fragment's order.
+    int tro[ND][2];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) tro[dt][x] = tr_swz_offset<D>(lane, 32 * dt, x);
+
     auto scores = [&](const bf16* Ks, f32x16 (&st)[NH][kNT]) {
 #pragma unroll
         for (int h = 0; h < NH; ++h)
@@ -213,8 +149,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
         for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int t = 0; t < kNT; ++t) {
-                const bf16x8 kf =
-                    __builtin_bit_cast(bf16x8, ld16(Ks + (32 * t + c) * S::KS + 16 * s + 8 * hh));
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, ld16(Ks + 32 * t * D + kro[s]));
 #pragma unroll
                 for (int h = 0; h < NH; ++h) st[h][t] = mfma32(kf, qf[h][s], st[h][t]);
             }
@@ -295,8 +230,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
             for (int t = 0; t < kNT; ++t)
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const bf16x8 vf = __builtin_bit_cast(
-                        bf16x8, ld16(Vt + (32 * dt + c) * S::VS + 16 * (2 * t + u) + 8 * hh));
+                    const bf16* vb = Vt + 16 * (2 * t + u) * D;
+                    const bf16x8 vf = join(lds_tr(vb + tro[dt][0]), lds_tr(vb + tro[dt][1]));
 #pragma unroll
                     for (int h = 0; h < NH; ++h) oacc[h][dt] = mfma32(vf, pf[h][t][u], oacc[h][dt]);
                 }
@@ -310,25 +245,27 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
     // Tile T lives in buffer T % 2, and both K(T+1) and V(T+1) are loaded during steps 2T, 2T+1
     // and stored after them, into the buffers of K(T-1) and V(T-1), released at the last barrier.
     auto ksub = [&](int j) {   // K rows of step j
-        return Kb + (((j - 1) >> 1) & 1) * S::K_ELEMS + ((j - 1) & 1) * kBC * S::KS;
+        return sm.k[((j - 1) >> 1) & 1] + ((j - 1) & 1) * kBC * D;
     };
-    auto vsub = [&](int j) { return Vb + ((j >> 1) & 1) * S::V_ELEMS + (j & 1) * kBC; };
+    auto vsub = [&](int j) { return sm.v[(j >> 1) & 1] + (j & 1) * kBC * D; };
     const int nlt = (kend + kLT - 1) / kLT;                       // V tiles
     const int nkt = kend > kBC ? (kend - kBC + kLT - 1) / kLT : 0;  // shifted K tiles
-    KRegs<D> kr;
-    VRegs vr;
+    auto load_k = [&](int T) {   // shifted K tile T: keys 64 T + 32 .. 64 T + 95
+        const int k0 = T * kLT + kBC;
+        dma_tile<D, kLT, kWaves>(K + (size_t)k0 * D, Lk - k0, sm.k[T & 1], w, lane);
+    };
+    auto load_v = [&](int T) {
+        const int k0 = T * kLT;
+        dma_tile<D, kLT, kWaves>(V + (size_t)k0 * D, Lk - k0, sm.v[T & 1], w, lane);
+    };
     f32x16 sa[NH][kNT], sb[NH][kNT];
     bf16x8 pf[NH][kNT][2];
     if (ntiles > 0) {
-        load_k<D>(kr, K, 0, Lk, tid);
-        load_v<D>(vr, V, 0, Lk, tid);
-        store_k_halves<D>(kr, Kb + S::K_ELEMS + kBC * S::KS, Kb, tid);   // keys 0..31, 32..63
-        store_v<D>(vr, Vb, tid);
-        if (kend > kLT) {
-            load_k<D>(kr, K, kLT, Lk, tid);
-            store_k_halves<D>(kr, Kb + kBC * S::KS, nullptr, tid);       // keys 64..95
-        }
+        dma_tile<D, kBC, kWaves>(K, Lk, sm.k[1] + kBC * D, w, lane);   // keys 0..31
+        load_v(0);
+        if (nkt > 0) load_k(0);
     }
+    wait_vmem();
     __syncthreads();
     if (ntiles > 0) {
         scores(ksub(0), sa);
@@ -337,23 +274,14 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
         bool moved[NH];
         update_max(sa, alpha, moved);   // O is zero: no rescale needed
     }
-    __syncthreads();   // keys 0..31 in buffer 1 are overwritten by K tile 1 after steps 0, 1
-    // No global load is outstanding here; saying so keeps the wait analysis from carrying
-    // prologue loads into the loop, where it would wait for every new tile load at once.
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();   // keys 0..31 in buffer 1 are overwritten by K tile 1 during steps 0, 1
 
-    // ---- steady state: step j with a successor ----------------------------------------------
-    // cur holds S(j) (row max already folded into m); nxt receives S(j+1).  Between the loads at
-    // the top and the rescale/stores at the bottom the step is one branch-free block, so the
-    // scheduler can interleave the MFMAs of S(j+1) and P(j) V(j) with the VALU work of steps j
-    // and j+1.  MASKN: step j+1 needs the causal / padding mask.  Even steps (j = 2T) issue the
-    // global loads of LDS tiles K(T+1) and V(T+1); odd steps store them and end with the barrier.
     auto step = [&](auto maskn, auto odd, int j, f32x16 (&cur)[NH][kNT],
                     f32x16 (&nxt)[NH][kNT]) {
         const int T = j >> 1;
-        if constexpr (!decltype(odd)::value) {
-            if (T + 1 < nkt) load_k<D>(kr, K, (T + 1) * kLT + kBC, Lk, tid);
-            if (T + 1 < nlt) load_v<D>(vr, V, (T + 1) * kLT, Lk, tid);
+        if constexpr (!decltype(odd)::value) {   // buffers (T+1)&1 were released at the last barrier
+            if (T + 1 < nkt) load_k(T + 1);
+            if (T + 1 < nlt) load_v(T + 1);
         }
         scores(ksub(j + 1), nxt);                           // MFMA ...
         exponentiate(cur, pf);                              // ... alongside VALU
@@ -364,9 +292,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
         update_max(nxt, alpha, moved);                      // ... alongside VALU
         rescale(alpha, moved);
         if constexpr (decltype(odd)::value) {
-            if (T + 1 < nkt) store_k<D>(kr, Kb + ((T + 1) & 1) * S::K_ELEMS, tid);
-            if (T + 1 < nlt) store_v<D>(vr, Vb + ((T + 1) & 1) * S::V_ELEMS, tid);
-            __syncthreads();
+            wait_vmem();       // this wave's share of tiles T+1 has landed
+            __syncthreads();   // tiles T+1 visible; buffers T&1 free
         }
     };
     // Steps below jfree need no mask for any row of the workgroup.
