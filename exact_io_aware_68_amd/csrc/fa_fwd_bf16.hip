@@ -28,7 +28,8 @@
 //     NH = 1 (two waves per SIMD): NH = 2 halves the LDS reads per flop but needs more
 //     registers than two waves per SIMD allow and measured slower at one wave per SIMD.
 //   * Scores are kept in log2 units: 2^(s * scale * log2 e - m) uses one FMA and v_exp_f32.
-//     The reference point m moves lazily (only when a score exceeds it by 2^8), which is exact
+//     The reference point m is the first step's row max and moves only when a step's P would
+//     sum past 2^16 in some lane, so the common step computes no row max at all; this is exact
 //     in real arithmetic because Otilde and l always share the same reference point.
 //   * Keys at or beyond key_lens[b] arrive as zeros (the DMA's buffer bound), so NaN padding
 //     cannot leak through 0 * NaN in P V, and are masked to -inf before the max.
@@ -46,7 +47,7 @@ constexpr int kBC = 32;         // keys per compute step
 constexpr int kNT = kBC / 32;   // 32-key blocks per compute step
 constexpr int kLT = 64;         // keys per LDS tile (two compute steps per barrier)
 constexpr int kThreads = 256;
-constexpr float kSlack = 8.f;   // lazy-rescale threshold, log2 units (P <= 256)
+constexpr float kSumCap = 65536.f;   // largest partial sum of P before m moves
 
 template <bool B>
 struct Flag {
@@ -171,55 +172,52 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
                     st[h][t][r] = hide ? kNegInf : st[h][t][r];
                 }
     };
-    // Row max of a new tile and the lazy move of the reference point.  Returns, per half,
-    // whether O must be rescaled by alpha before the tile's P V product.
-    auto update_max = [&](const f32x16 (&st)[NH][kNT], float (&alpha)[NH], bool (&moved)[NH]) {
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            float mx = kNegInf;
-#pragma unroll
-            for (int t = 0; t < kNT; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[h][t][r]);
-            mx = max_with_partner(mx) * C;
-            moved[h] = __builtin_amdgcn_ballot_w64(mx > m[h] + kSlack) != 0;
-            const float mnew = moved[h] ? fmaxf(m[h], mx) : m[h];
-            alpha[h] = mnew == kNegInf ? 1.f : exp2_hw(m[h] - mnew);
-            m[h] = mnew;
-            lsum[h] *= alpha[h];
-        }
-    };
-    auto rescale = [&](const float (&alpha)[NH], const bool (&moved)[NH]) {
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-            if (moved[h]) {
-#pragma unroll
-                for (int i = 0; i < ND; ++i) oacc[h][i] *= alpha[h];
-            }
-    };
     // P = 2^(s C - m) for both halves, row sums, bf16 B operands (t, u): keys 32t + 16u + ...
-    auto exponentiate = [&](f32x16 (&st)[NH][kNT], bf16x8 (&pf)[NH][kNT][2]) {
+    // The reference point m is not kept at the running max: it is set from the first step's
+    // scores and moves only when this step's P would sum past kSumCap in some lane of the wave
+    // (which also catches an overflow to inf).  Then m moves to the row max so far, O and l are
+    // rescaled, and the step's P is recomputed against it.  In real arithmetic the result does
+    // not depend on the reference point, since O and l always share it; the cap keeps every P
+    // and partial sum far from the fp32 and bf16 limits.  The common step computes no row max.
+    auto exponentiate = [&](const f32x16 (&st)[NH][kNT], bf16x8 (&pf)[NH][kNT][2]) {
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
-            const float muse = m[h] == kNegInf ? 0.f : m[h];
-            float rs = 0.f;
+            float pe[kNT][16];
+            float rs;
+            auto expo = [&]() {
+                const float muse = m[h] == kNegInf ? 0.f : m[h];
+                rs = 0.f;
 #pragma unroll
-            for (int t = 0; t < kNT; ++t)
+                for (int t = 0; t < kNT; ++t)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = exp2_hw(__builtin_fmaf(st[h][t][r], C, -muse));
-                    st[h][t][r] = e;
-                    rs += e;
-                }
+                    for (int r = 0; r < 16; ++r) {
+                        pe[t][r] = exp2_hw(__builtin_fmaf(st[h][t][r], C, -muse));
+                        rs += pe[t][r];
+                    }
+            };
+            expo();
+            if (__builtin_amdgcn_ballot_w64(!(rs <= kSumCap)) != 0) {
+                float mx = kNegInf;
+#pragma unroll
+                for (int t = 0; t < kNT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[h][t][r]);
+                const float mnew = fmaxf(m[h], max_with_partner(mx) * C);
+                const float alpha = mnew == kNegInf ? 1.f : exp2_hw(m[h] - mnew);
+                m[h] = mnew;
+                lsum[h] *= alpha;
+#pragma unroll
+                for (int i = 0; i < ND; ++i) oacc[h][i] *= alpha;
+                expo();
+            }
             lsum[h] += rs;
 #pragma unroll
             for (int t = 0; t < kNT; ++t)
 #pragma unroll
                 for (int u = 0; u < 2; ++u)
-                    pf[h][t][u] = to_bf16x8(st[h][t][8 * u + 0], st[h][t][8 * u + 1],
-                                            st[h][t][8 * u + 2], st[h][t][8 * u + 3],
-                                            st[h][t][8 * u + 4], st[h][t][8 * u + 5],
-                                            st[h][t][8 * u + 6], st[h][t][8 * u + 7]);
+                    pf[h][t][u] = to_bf16x8(pe[t][8 * u + 0], pe[t][8 * u + 1], pe[t][8 * u + 2],
+                                            pe[t][8 * u + 3], pe[t][8 * u + 4], pe[t][8 * u + 5],
+                                            pe[t][8 * u + 6], pe[t][8 * u + 7]);
         }
     };
     // O^T += V^T P^T for both halves: each V^T fragment (row d = 32 dt + c) feeds two MFMAs.
@@ -270,9 +268,17 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
     if (ntiles > 0) {
         scores(ksub(0), sa);
         if (need_mask(0)) mask(0, sa);
-        float alpha[NH];
-        bool moved[NH];
-        update_max(sa, alpha, moved);   // O is zero: no rescale needed
+        // The reference point starts at the row max of the first step (finite for every row:
+        // key 0 is valid for all of them when Lk >= 1).
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            float mx = kNegInf;
+#pragma unroll
+            for (int t = 0; t < kNT; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[h][t][r]);
+            m[h] = max_with_partner(mx) * C;
+        }
     }
     __syncthreads();   // keys 0..31 in buffer 1 are overwritten by K tile 1 during steps 0, 1
 
@@ -286,11 +292,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
         scores(ksub(j + 1), nxt);                           // MFMA ...
         exponentiate(cur, pf);                              // ... alongside VALU
         if constexpr (decltype(maskn)::value) mask(j + 1, nxt);
-        pv(vsub(j), pf);                                    // MFMA ...
-        float alpha[NH];
-        bool moved[NH];
-        update_max(nxt, alpha, moved);                      // ... alongside VALU
-        rescale(alpha, moved);
+        pv(vsub(j), pf);
         if constexpr (decltype(odd)::value) {
             wait_vmem();       // this wave's share of tiles T+1 has landed
             __syncthreads();   // tiles T+1 visible; buffers T&1 free

@@ -131,6 +131,29 @@ def test_forward_is_bitwise_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_scores_rising_and_falling_along_keys(causal, d):
+    """Head 0: scores rise by about 140-200 (log2 units) from the first keys to the last, so
+    exponentials taken against the first keys' maximum would overflow fp32 and the kernel's
+    reference point has to move many times.  Head 1: scores fall just as far, so the later
+    exponentials underflow to zero."""
+    B, N = 1, 700
+    print(f"\nfwd rising/falling scores d={d} causal={causal}", flush=True)
+    g = torch.Generator().manual_seed(77 + d)
+    q = 1.0 + 0.1 * torch.randn(B, 2, N, d, generator=g)
+    ramp = torch.linspace(0.0, 12.0, N).view(1, 1, N, 1)
+    k = torch.cat([ramp, 12.0 - ramp], dim=1) + 0.1 * torch.randn(B, 2, N, d, generator=g)
+    v = torch.randn(B, 2, N, d, generator=g)
+    x = {"q": q.to(torch.bfloat16), "k": k.to(torch.bfloat16), "v": v.to(torch.bfloat16),
+         "scale": float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32)), "key_lens": None}
+    o, lse = run_fwd(x, causal)
+    O, LSE = attn_fwd(x["q"], x["k"], x["v"], x["scale"], causal)
+    assert np.max(LSE[:, 0]) > 90.0   # the rise really is past the fp32 exponent range
+    check_close("O", np64(o), O, TOL_BF16_MAX, TOL_BF16_MEAN)
+    check_close("LSE", np64(lse), LSE, TOL_LSE)
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 def _sample_rows(w, n_rand, seed):
