@@ -30,12 +30,16 @@ DEVICE_FLAGS = [
 ]
 
 
-# Per-source extra flags.  The forward and the dQ kernel keep their MFMA accumulators in ordinary
-# VGPRs: their score tiles are post-processed by VALU code every step and they fit 2 waves per
-# SIMD that way.
+# Per-source extra flags.  Every bf16 kernel keeps its MFMA results in ordinary VGPRs: the score
+# tiles are post-processed by VALU code every step.  Left to its heuristics the compiler picks
+# accumulation registers for all MFMAs of a kernel that needs more than 256 registers (dK/dV),
+# and then copies the score tiles out and the long-lived dK, dV accumulators in and out of them
+# on every iteration (about 240 copies per 64 MFMAs); with this flag it spills a few loop-
+# invariant values to accumulation registers instead.
 FILE_FLAGS = {
     "fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "fa_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fa_bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
