@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
                 // Phase fences keep the scheduler from hoisting the next phase's LDS reads
                 // across this one, which would push the live registers past the VGPR file.
                 __builtin_amdgcn_sched_barrier(0);
-                // P = 2^(S C - LSE2) and scale * dS = scale * P (dP - D).
+                // P = 2^(S C - LSE2) and dS = P (dP - D) (the scale of dK is applied at the end).
                 const bool need_mask = (CAUSAL && kw0 + 31 > i0) || (kw0 + 32 > Lk);
 #pragma unroll
                 for (int q2 = 0; q2 < 2; ++q2)
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
                                 pv = hide ? 0.f : pv;
                             }
                             sa[q2][r] = pv;
-                            pa[q2][r] = pv * (pa[q2][r] - d4[x]) * p.scale;
+                            pa[q2][r] = pv * (pa[q2][r] - d4[x]);
                         }
                     }
                 bf16x8 pf[4], sf[4];
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
                                       pa[q2][o8 + 4], pa[q2][o8 + 5], pa[q2][o8 + 6], pa[q2][o8 + 7]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                // dV^T += dO^T P, dK^T += Q^T (scale dS): A = one d-column over 8 query rows.
+                // dV^T += dO^T P, dK^T += Q^T dS: A = one d-column over 8 query rows.
                 // Same read-ahead as above, one (dt, u) pair of products at a time.
                 bf16x8 ao, aq;
                 auto rdt = [&](int g, bf16x8& o_, bf16x8& q_) {
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
         }
     }
 
-    // dK (scale already folded into dS), dV: lane = key, C rows = d.
+    // dK = scale dS^T Q (the scale is applied once here), dV: lane = key, C rows = d.
     if (key < N) {
         float* __restrict__ dK = p.dk + kvbase + (size_t)key * D;
         float* __restrict__ dV = p.dv + kvbase + (size_t)key * D;
@@ -289,7 +289,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int dcol = 32 * dt + 8 * g + 4 * hh;
-                float4 kv = {dka[dt][4 * g], dka[dt][4 * g + 1], dka[dt][4 * g + 2], dka[dt][4 * g + 3]};
+                float4 kv = {dka[dt][4 * g] * p.scale, dka[dt][4 * g + 1] * p.scale,
+                             dka[dt][4 * g + 2] * p.scale, dka[dt][4 * g + 3] * p.scale};
                 float4 vv = {dva[dt][4 * g], dva[dt][4 * g + 1], dva[dt][4 * g + 2], dva[dt][4 * g + 3]};
                 *reinterpret_cast<float4*>(dK + dcol) = kv;
                 *reinterpret_cast<float4*>(dV + dcol) = vv;
