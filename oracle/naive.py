@@ -43,7 +43,7 @@ import numpy as np
 
 __all__ = [
     "to64", "kv_head_of", "visible_mask", "attn_fwd", "attn_fwd_rows",
-    "attn_bwd", "attn_bwd_heads", "score_rows",
+    "attn_bwd", "attn_bwd_heads", "score_rows", "attn_decode",
 ]
 
 
@@ -130,6 +130,37 @@ def attn_fwd(q, k, v, scale: float, causal: bool = False, key_lens=None,
             with np.errstate(divide="ignore"):
                 LSE[b, h, rows] = np.where(np.isfinite(m), m + np.log(np.where(l > 0, l, 1.0)),
                                            -np.inf)
+    return O, LSE
+
+
+def attn_decode(q, k, v, scale: float, key_lens=None):
+    """Decode-shaped forward: Nq query rows per head against Nk keys, Nq and Nk independent.
+
+    q: [B, Hq, Nq, d]; k, v: [B, Hkv, Nk, d].  Every query row of batch b sees the keys j < L_b
+    (L_b = key_lens[b], default Nk) and no causal mask applies: the rows stand for new tokens
+    attending to a cache of L_b keys.  The guide page ("FlashAttention", Key takeaways) says
+    decode wants another mapping of the same math; the mask reading is this module's.
+    Returns (O [B, Hq, Nq, d], LSE [B, Hq, Nq]), fp64.
+    """
+    q, k, v = to64(q), to64(k), to64(v)
+    B, Hq, Nq, _ = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    lens = _lens(key_lens, B, Nk)
+    O = np.zeros((B, Hq, Nq, v.shape[-1]))
+    LSE = np.zeros((B, Hq, Nq))
+    rows = np.arange(Nq)
+    for b in range(B):
+        L = lens[b]
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            K, V = k[b, g, :L], v[b, g, :L]
+            s = score_rows(q[b, h], K, scale)
+            P, m, l = _softmax_rows(s, visible_mask(rows, L, False))
+            O[b, h] = P @ V
+            with np.errstate(divide="ignore"):
+                LSE[b, h] = np.where(np.isfinite(m), m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
     return O, LSE
 
 
