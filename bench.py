@@ -74,6 +74,17 @@ def bwd_bytes_compulsory(B, Hq, Hkv, N, d, elem=2):
     return reads + d_rw + writes
 
 
+def bwd_kernel_bytes_compulsory(B, Hq, Hkv, N, d, elem=2):
+    """Per backward kernel: prep reads O, dO, LSE and writes D and the base-2 LSE; dK/dV reads
+    Q, dO, K, V and both statistics and writes fp32 dK, dV; dQ reads the same and writes fp32 dQ."""
+    q = B * Hq * N * d * elem
+    kv = B * Hkv * N * d * elem
+    rows = B * Hq * N * 4
+    return {"bwd_prep": 2 * q + rows + 2 * rows,
+            "bwd_dkdv": 2 * q + 2 * kv + 2 * rows + 2 * B * Hkv * N * d * 4,
+            "bwd_dq": 2 * q + 2 * kv + 2 * rows + B * Hq * N * d * 4}
+
+
 def naive_bytes(B, Hq, N, elem=2):
     """Naive attention's score traffic alone: write S, read S, write P, read P (elem bytes)."""
     return 4 * N * N * elem * B * Hq
@@ -143,7 +154,7 @@ def traffic_summary(d, workload, cmd_note):
     import fa_inputs as fi
     w = fi.WORKLOADS[workload]
     comp = {"fwd_bf16": fwd_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d),
-            "bwd_prep": None, "bwd_dkdv": None, "bwd_dq": None}
+            **bwd_kernel_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d)}
     rows = []
     for k in ("fwd_bf16", "bwd_prep", "bwd_dkdv", "bwd_dq"):
         if k not in f["bench_FETCH_SIZE"]:
@@ -167,7 +178,9 @@ FETCH_SIZE = {f['copy_FETCH_SIZE']['copy']:.0f} KiB and WRITE_SIZE =
 {f['copy_WRITE_SIZE']['copy']:.0f} KiB per dispatch, so FETCH_SIZE is scaled by {fr:.3f} and
 WRITE_SIZE by {fw:.3f}.  `bytes/launch` = calibrated FETCH + WRITE; `vs compulsory` divides by
 the tiled IO count (read Q, K, V once, write O and LSE once).  `src` is the hash bench.py
-compares with the kernel's current sources: a stale row reads as unmeasured.
+compares with the kernel's current sources: a stale row reads as unmeasured.  Compulsory bytes
+of the backward kernels: prep reads O, dO, LSE and writes D and the base-2 LSE; dK/dV reads Q,
+dO, K, V and both row statistics and writes fp32 dK, dV; dQ reads the same and writes fp32 dQ.
 
 | kernel | src | FETCH_SIZE KiB | WRITE_SIZE KiB | calibrated MiB | bytes/launch | vs compulsory |
 |---|---|---|---|---|---|---|
