@@ -13,6 +13,8 @@ The functions carry the C names (see include/fa.h for the full contract):
     fa_bwd_dq(q, k, v, dO, dq, workspace, ...)                       (the stages of fa_bwd)
     fa_bwd_workspace_size, fa_fwd_kernel_name, fa_bwd_dkdv_kernel_name, fa_bwd_dq_kernel_name,
     fa_status_str, fa_abi_version
+    fa_fwd_splitkv(q, k, v, *, scale, key_lens, num_splits, o, lse)  -> (o, lse)   (decode shapes)
+    fa_fwd_splitkv_splits, fa_fwd_splitkv_workspace_size
 
 Tensors are [B, H, N, d] contiguous ("BHND"); q/k/v/o/dO are bf16 (d in {64, 128}) or fp32
 (forward only, d <= 128); lse is fp32 [B, Hq, N]; key_lens int32 [B] on the device; gradients
@@ -28,6 +30,7 @@ __all__ = [
     "FAError", "lib_path", "load", "fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq",
     "fa_bwd_workspace_size", "fa_fwd_kernel_name", "fa_bwd_dkdv_kernel_name",
     "fa_bwd_dq_kernel_name", "fa_status_str", "fa_abi_version", "FA_F32", "FA_BF16",
+    "fa_fwd_splitkv", "fa_fwd_splitkv_splits", "fa_fwd_splitkv_workspace_size",
 ]
 
 FA_F32, FA_BF16 = 0, 1
@@ -67,6 +70,12 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_dq.restype = I
     lib.fa_bwd_workspace_size.argtypes = [I, I, I, I]
     lib.fa_bwd_workspace_size.restype = Z
+    lib.fa_fwd_splitkv.argtypes = [P, P, P, P, P, P, P, Z, I, I, I, I, I, I, F, I, I, P]
+    lib.fa_fwd_splitkv.restype = I
+    lib.fa_fwd_splitkv_splits.argtypes = [I, I, I, I, I, I]
+    lib.fa_fwd_splitkv_splits.restype = I
+    lib.fa_fwd_splitkv_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.fa_fwd_splitkv_workspace_size.restype = Z
     for name in ("fa_fwd_kernel_name", "fa_bwd_dkdv_kernel_name", "fa_bwd_dq_kernel_name"):
         getattr(lib, name).argtypes = [I, I, I, I]
         getattr(lib, name).restype = ctypes.c_char_p
@@ -216,3 +225,44 @@ def fa_bwd(q, k, v, o, dO, lse, *, scale: float | None = None, causal: bool = Fa
                        int(causal), _dtype_code(q), _stream(stream, q.device))
     _check("fa_bwd", st)
     return dq, dk, dv
+
+
+def fa_fwd_splitkv_splits(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, num_splits: int = 0) -> int:
+    return int(load().fa_fwd_splitkv_splits(B, Hq, Hkv, Nq, Nk, num_splits))
+
+
+def fa_fwd_splitkv_workspace_size(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
+                                  num_splits: int = 0) -> int:
+    return int(load().fa_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits))
+
+
+def fa_fwd_splitkv(q, k, v, *, scale: float | None = None, key_lens=None, num_splits: int = 0,
+                   o=None, lse=None, want_lse: bool = True, workspace=None, stream=None):
+    """Split-KV forward for decode shapes: q [B, Hq, Nq, d] against k, v [B, Hkv, Nk, d]; every
+    query row sees keys [0, key_lens[b]).  Returns (o, lse); lse is None if not wanted."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q, k, v must be 4-D [B, H, N, d] with k and v of one shape")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k/v shape does not match q")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    if key_lens is not None and key_lens.dtype != torch.int32:
+        raise ValueError("key_lens must be int32")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = fa_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits)
+        workspace = torch.empty(max(16, n), dtype=torch.uint8, device=q.device)
+    st = load().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(key_lens),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(), B,
+                               Hq, Hkv, Nq, Nk, d,
+                               ctypes.c_float(_default_scale(d) if scale is None else scale),
+                               int(num_splits), _dtype_code(q), _stream(stream, q.device))
+    _check("fa_fwd_splitkv", st)
+    return o, lse

@@ -220,4 +220,81 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
     return launched(fa::launch_bwd_dq_bf16(p, s));
 }
 
+// ---- split-KV forward (decode shapes) ----------------------------------------------------------
+
+// Key ranges: with num_splits = 0, enough ranges that the (batch, kv-head, row tile, range)
+// workgroups fill the GPU about four times over; each range a multiple of 128 keys (4 waves of
+// 32-key steps).  Returns the number of ranges and their length in keys.
+static void splitkv_plan(int B, int Hq, int Hkv, int Nq, int Nk, int req, int* splits, int* kps) {
+    const long long rows = (long long)(Hq / Hkv) * Nq;
+    const long long base = (long long)B * Hkv * ((rows + 31) / 32);
+    const long long most = (Nk + 127) / 128 > 0 ? (Nk + 127) / 128 : 1;
+    long long s = req > 0 ? req : (1024 + base - 1) / (base > 0 ? base : 1);
+    if (s < 1) s = 1;
+    if (s > most) s = most;
+    long long k = ((Nk + s - 1) / s + 127) / 128 * 128;
+    if (k < 128) k = 128;
+    s = (Nk + k - 1) / k;
+    if (s < 1) s = 1;
+    *splits = (int)s;
+    *kps = (int)k;
+}
+
+static fa_status check_splitkv_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits) {
+    if (B < 0 || Nq < 0 || Nk < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || num_splits < 0)
+        return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_GQA;
+    if ((long double)B * Hq * Nq * d > 9.0e18L || (long double)B * Hkv * Nk * d > 9.0e18L)
+        return FA_ERR_SHAPE;
+    int splits, kps;
+    splitkv_plan(B, Hq, Hkv, Nq, Nk, num_splits, &splits, &kps);
+    const long double rows = (long double)(Hq / Hkv) * Nq;
+    if ((long double)B * Hkv * ((rows + 31) / 32 + 1) * splits > 4.0e9L) return FA_ERR_SHAPE;
+    if ((long double)B * Hq * Nq * (d / 8 + 1) > 4.0e9L * 256) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+int fa_fwd_splitkv_splits(int B, int Hq, int Hkv, int Nq, int Nk, int num_splits) {
+    if (check_splitkv_shape(B, Hq, Hkv, Nq, Nk, 8, num_splits) != FA_OK) return 0;
+    int splits, kps;
+    splitkv_plan(B, Hq, Hkv, Nq, Nk, num_splits, &splits, &kps);
+    return splits;
+}
+
+size_t fa_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                     int num_splits) {
+    if (check_splitkv_shape(B, Hq, Hkv, Nq, Nk, d, num_splits) != FA_OK) return 0;
+    int splits, kps;
+    splitkv_plan(B, Hq, Hkv, Nq, Nk, num_splits, &splits, &kps);
+    return (size_t)splits * (size_t)B * (size_t)Hq * (size_t)Nq * (size_t)(d + 1) * sizeof(float);
+}
+
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const int32_t* key_lens, void* workspace, size_t workspace_bytes, int B,
+                         int Hq, int Hkv, int Nq, int Nk, int d, float scale, int num_splits,
+                         fa_dtype dtype, void* stream) {
+    if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_DTYPE;
+    fa_status st = check_splitkv_shape(B, Hq, Hkv, Nq, Nk, d, num_splits);
+    if (st != FA_OK) return st;
+    if (dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if ((st = check_scale(scale)) != FA_OK) return st;
+    if (B == 0 || Nq == 0) return FA_OK;   // no query row: nothing to compute
+    if (!q || !o || (Nk > 0 && (!k || !v))) return FA_ERR_NULL;
+    if (!workspace ||
+        workspace_bytes < fa_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits))
+        return FA_ERR_WORKSPACE;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+        misaligned(lse, 4) || misaligned(key_lens, 4) || misaligned(workspace, 16))
+        return FA_ERR_ALIGN;
+    if ((st = device_ready()) != FA_OK) return st;
+    int splits, kps;
+    splitkv_plan(B, Hq, Hkv, Nq, Nk, num_splits, &splits, &kps);
+    const size_t rows = (size_t)B * Hq * Nq;
+    float* opart = static_cast<float*>(workspace);
+    fa::SplitParams p{q, k, v, o, lse, key_lens, opart, opart + (size_t)splits * rows * d,
+                      B, Hq, Hkv, Nq, Nk, d, splits, kps, scale};
+    return launched(fa::launch_splitkv_bf16(p, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -36,7 +36,26 @@ struct BwdParams {
     int causal;
 };
 
+// Split-KV forward for decode shapes: Nq query rows per q-head against Nk keys, no causal mask.
+// The keys are cut into `splits` ranges of `kps` keys (a multiple of 128); the first kernel
+// writes each range's normalised partial output and natural-log LSE into the workspace, the
+// second merges them.
+struct SplitParams {
+    const void* q;            // [B][Hq][Nq][d] bf16
+    const void* k;            // [B][Hkv][Nk][d] bf16
+    const void* v;
+    void* o;                  // [B][Hq][Nq][d] bf16
+    float* lse;               // [B][Hq][Nq] fp32, may be null
+    const int32_t* key_lens;  // may be null
+    float* opart;             // workspace: [splits][B*Hq*Nq][d] fp32
+    float* lpart;             // workspace: [splits][B*Hq*Nq] fp32
+    int B, Hq, Hkv, Nq, Nk, d;
+    int splits, kps;
+    float scale;
+};
+
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+hipError_t launch_splitkv_bf16(const SplitParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_prep_bf16(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16(const BwdParams& p, hipStream_t stream);

@@ -1,0 +1,298 @@
+// fa_splitkv.hip — split-KV forward for decode shapes (few query rows, many keys), gfx950.
+//
+// Method: the same exact attention as the forward (tutorial page "Flash attention and efficient
+// attention", "Derivation: Incremental Softmax"), mapped for decode as the guide page
+// ("FlashAttention", Key takeaways) says decode wants: with a handful of query rows per head
+// there is no query tile to parallelise over, so the KEYS are split instead.  Each key range
+// produces a normalised partial output O_p and its log-sum-exp LSE_p; a second kernel merges
+// them with the tutorial's step-3 identity, LSE = log sum_p e^{LSE_p}, O = sum_p e^{LSE_p - LSE} O_p.
+//
+// Mapping on CDNA4:
+//   * One workgroup per (batch, kv-head, 32-row tile of that kv-head's rows, key range).  The
+//     rows of a kv-head are all (q-head of its group, query) pairs, so grouped-query heads share
+//     one K/V stream: with Nq = 1 and 4 q-heads per kv-head, 4 of the 32 MFMA columns are real.
+//     The kernel is bound by HBM (every K and V byte is read once), not by the MFMA.
+//   * 4 waves per workgroup split the range's 32-key steps round-robin; each wave carries its own
+//     online-softmax state and the four are merged through LDS at the end.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 takes its K operands straight from global memory
+//     (each lane loads the 16-byte chunks of its key row it needs; no LDS).  V rows are loaded
+//     into registers one step ahead, stored into the wave's own swizzled LDS tile and read back
+//     transposed (ds_read_b64_tr_b16) as the A operand of O^T += V^T P^T.
+//   * Keys at or beyond key_lens[b] arrive as zeros through the buffer bound and are masked.
+//   * Reference point of the exponentials: the row max of each wave's first step, moved only
+//     when a step's exponentials would sum past 2^16 (as in the forward).
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBC = 32;              // keys per step
+constexpr int kRows = 32;            // query rows per row tile (the MFMA's column count)
+constexpr float kSumCap = 65536.f;   // largest partial sum of P before the reference point moves
+
+template <int D>
+struct CombineLds {
+    float o[kWaves][kRows][D + 4];   // each wave's unnormalised output (padded rows)
+    float m[kWaves][kRows];          // its reference point (log2 units)
+    float l[kWaves][kRows];          // its sum of exponentials
+};
+
+template <int D>
+union SplitLds {
+    bf16 v[kWaves][kBC * D];   // one swizzled V tile per wave
+    CombineLds<D> c;           // reused after the key loop
+};
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void splitkv_bf16_kernel(SplitParams p) {
+    constexpr int NS = D / 16;             // MFMAs of one S^T step
+    constexpr int ND = D / 32;             // 32-column blocks of O
+    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    constexpr int VCH = kBC * CPR / 64;    // V chunks per lane per step
+    __shared__ __attribute__((aligned(1024))) SplitLds<D> sm;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
+    const int G = p.Hq / p.Hkv, R = G * p.Nq, nrt = (R + kRows - 1) / kRows;
+    int x = blockIdx.x;
+    const int split = x % p.splits;
+    x /= p.splits;
+    const int rt = x % nrt;
+    x /= nrt;
+    const int hkv = x % p.Hkv, b = x / p.Hkv;
+
+    int Lk = p.Nk;
+    if (p.key_lens) Lk = min(max(p.key_lens[b], 0), p.Nk);
+    const int ks = split * p.kps;
+    const int ke = min(ks + p.kps, Lk);                     // key range [ks, ke), maybe empty
+    const int nsteps = ke > ks ? (ke - ks + kBC - 1) / kBC : 0;
+
+    // This lane's row: (q-head g of the group, query qi); rows >= R are padding.
+    const int r = rt * kRows + c;
+    const bool real = r < R;
+    const int g = real ? r / p.Nq : 0, qi = real ? r - g * p.Nq : 0;
+    const size_t rowg = ((size_t)b * p.Hq + hkv * G + g) * p.Nq + qi;
+    const size_t kvbase = (size_t)(b * p.Hkv + hkv) * p.Nk * D;
+    const bf16* __restrict__ K = (const bf16*)p.k + kvbase;
+    const bf16* __restrict__ V = (const bf16*)p.v + kvbase;
+    const float C = p.scale * kLog2e;
+
+    // Q fragments: B operands of S^T = K Q^T (lane = row, slots = 8 consecutive d).
+    bf16x8 qf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        u32x4 z = {0, 0, 0, 0};
+        if (real) z = ld16((const bf16*)p.q + rowg * D + 16 * s + 8 * hh);
+        qf[s] = __builtin_bit_cast(bf16x8, z);
+    }
+
+    f32x16 oacc[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i) oacc[i] = f32x16{};
+    float m = kNegInf, lsum = 0.f;
+
+    // Transpose reads of V^T: columns 32 dt + c, keys 16u + the C fragment's order.
+    int tro[ND][2];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int xx = 0; xx < 2; ++xx) tro[dt][xx] = tr_swz_offset<D>(lane, 32 * dt, xx);
+    bf16* const Vs = sm.v[w];
+
+    // Loads of step t (keys ks + 32 t ..): the lane's K row chunks (A operands of S^T) and V
+    // chunks (contiguous mapping); rows >= Lk arrive as zeros.  The row counts are uniform per
+    // wave; readfirstlane keeps the resources in scalar registers.
+    auto load = [&](int t, bf16x8 (&kf)[NS], u32x4 (&vr)[VCH]) {
+        const int k0 = ks + kBC * t;
+        const uint32_t nb =
+            (uint32_t)__builtin_amdgcn_readfirstlane(max(min(Lk - k0, kBC), 0)) * D * 2;
+        const rsrc_t rk = make_rsrc(K + (size_t)k0 * D, nb);
+        const rsrc_t rv = make_rsrc(V + (size_t)k0 * D, nb);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            kf[s] = __builtin_bit_cast(bf16x8, buf_ld16(rk, (c * D + 16 * s + 8 * hh) * 2));
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) vr[i] = buf_ld16(rv, (lane + 64 * i) * 16);
+    };
+
+    bf16x8 kc[NS];
+    u32x4 vc[VCH];
+    if (w < nsteps) load(w, kc, vc);
+    for (int t = w; t < nsteps; t += kWaves) {
+        // V tile of step t into this wave's LDS tile (its previous contents were last read by
+        // this wave's previous step, earlier in program order); then the loads of the wave's
+        // next step are issued into the same V registers, so they fly during this step.
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+            const int id = lane + 64 * i;
+            st16(Vs + swz_at<D>(id / CPR, 8 * (id % CPR)), vc[i]);
+        }
+        bf16x8 kn[NS];
+        const bool more = t + kWaves < nsteps;
+        if (more) load(t + kWaves, kn, vc);
+        f32x16 st = f32x16{};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) st = mfma32(kc[s], qf[s], st);
+        const int k0 = ks + kBC * t;
+        if (k0 + kBC > Lk) {   // C row rr -> key k0 + 8(rr/4) + 4hh + rr%4
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int key = k0 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+                st[rr] = key >= Lk ? kNegInf : st[rr];
+            }
+        }
+        auto rowmax = [&]() {
+            float mx = kNegInf;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, st[rr]);
+            return max_with_partner(mx) * C;
+        };
+        if (t == w) m = rowmax();   // the first step holds key k0 < Lk: m is finite
+        float pe[16], rs;
+        auto expo = [&]() {
+            rs = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                pe[rr] = exp2_hw(__builtin_fmaf(st[rr], C, -m));
+                rs += pe[rr];
+            }
+        };
+        expo();
+        if (__builtin_amdgcn_ballot_w64(!(rs <= kSumCap)) != 0) {
+            const float mnew = fmaxf(m, rowmax());
+            const float alpha = exp2_hw(m - mnew);
+            m = mnew;
+            lsum *= alpha;
+#pragma unroll
+            for (int i = 0; i < ND; ++i) oacc[i] *= alpha;
+            expo();
+        }
+        lsum += rs;
+        bf16x8 pf[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            pf[u] = to_bf16x8(pe[8 * u], pe[8 * u + 1], pe[8 * u + 2], pe[8 * u + 3], pe[8 * u + 4],
+                              pe[8 * u + 5], pe[8 * u + 6], pe[8 * u + 7]);
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const bf16* vb = Vs + 16 * u * D;
+                const bf16x8 vf = join(lds_tr(vb + tro[dt][0]), lds_tr(vb + tro[dt][1]));
+                oacc[dt] = mfma32(vf, pf[u], oacc[dt]);
+            }
+        if (more) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) kc[s] = kn[s];
+        }
+    }
+
+    // ---- merge the four waves' states (same rows, disjoint keys) through LDS --------------
+    __syncthreads();   // every wave is done with its V tile
+    const float lrow = sum_with_partner(lsum);
+    if (hh == 0) {
+        sm.c.m[w][c] = m;
+        sm.c.l[w][c] = lrow;
+    }
+    // O^T C fragment: column c = row, register (dt, 4j + i) -> d = 32 dt + 8 j + 4 hh + i.
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<f32x4*>(&sm.c.o[w][c][32 * dt + 8 * j + 4 * hh]) =
+                f32x4{oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]};
+    __syncthreads();
+
+    constexpr int TPR = kThreads / kRows;   // threads per row
+    constexpr int DPT = D / TPR;            // columns per thread (16 or 8)
+    const int row = tid / TPR, d0 = (tid % TPR) * DPT;
+    const int rr = rt * kRows + row;
+    if (rr < R) {
+        float M = kNegInf;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.c.m[ww][row]);
+        float wt[kWaves], Ls = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            const float mw = sm.c.m[ww][row];
+            wt[ww] = mw == kNegInf ? 0.f : exp2_hw(mw - M);
+            Ls += wt[ww] * sm.c.l[ww][row];
+        }
+        const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+        const int g2 = rr / p.Nq, q2 = rr - g2 * p.Nq;
+        const size_t rows = (size_t)p.B * p.Hq * p.Nq;
+        const size_t rg = ((size_t)b * p.Hq + hkv * G + g2) * p.Nq + q2;
+        float* dst = p.opart + ((size_t)split * rows + rg) * D + d0;
+#pragma unroll
+        for (int j = 0; j < DPT; j += 4) {
+            f32x4 o4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float a = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < kWaves; ++ww) a += wt[ww] * sm.c.o[ww][row][d0 + j + i];
+                o4[i] = a * inv;
+            }
+            *reinterpret_cast<f32x4*>(dst + j) = o4;
+        }
+        if (d0 == 0)
+            p.lpart[(size_t)split * rows + rg] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : kNegInf;
+    }
+}
+
+// Merge of the key ranges' partial results: one thread per (row, 8 columns).
+template <int D>
+__global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitParams p) {
+    constexpr int CH = D / 8;
+    const long long rows = (long long)p.B * p.Hq * p.Nq;
+    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= rows * CH) return;
+    const long long row = gid / CH;
+    const int ch = (int)(gid - row * CH);
+    float M = kNegInf;
+    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.lpart[s * rows + row]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    if (M != kNegInf) {
+        for (int s = 0; s < p.splits; ++s) {
+            const float wgt = exp2_hw((p.lpart[s * rows + row] - M) * kLog2e);   // 0 for -inf
+            L += wgt;
+            const f32x4* src = reinterpret_cast<const f32x4*>(p.opart + (s * rows + row) * D + 8 * ch);
+            const f32x4 a = src[0], bq = src[1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[i] += wgt * a[i];
+                acc[4 + i] += wgt * bq[i];
+            }
+        }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    bf16* o = (bf16*)p.o + row * D + 8 * ch;
+    *reinterpret_cast<bf16x8*>(o) = to_bf16x8(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv,
+                                              acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    if (ch == 0 && p.lse) p.lse[row] = L > 0.f ? M + logf(L) : kNegInf;
+}
+
+hipError_t launch_splitkv_bf16(const SplitParams& p, hipStream_t stream) {
+    const int G = p.Hq / p.Hkv, R = G * p.Nq, nrt = (R + kRows - 1) / kRows;
+    dim3 grid1((unsigned)((long long)p.B * p.Hkv * nrt * p.splits)), block(kThreads);
+    const long long n2 = (long long)p.B * p.Hq * p.Nq * (p.d / 8);
+    dim3 grid2((unsigned)((n2 + 255) / 256)), block2(256);
+    if (p.d == 128) {
+        hipLaunchKernelGGL(splitkv_bf16_kernel<128>, grid1, block, 0, stream, p);
+        hipLaunchKernelGGL(splitkv_merge_kernel<128>, grid2, block2, 0, stream, p);
+    } else {
+        hipLaunchKernelGGL(splitkv_bf16_kernel<64>, grid1, block, 0, stream, p);
+        hipLaunchKernelGGL(splitkv_merge_kernel<64>, grid2, block2, 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fa

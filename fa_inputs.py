@@ -94,6 +94,49 @@ def make(w: Workload, want_do: bool | None = None) -> dict:
     return out
 
 
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Decode shape: Nq query rows per q-head against Nk cached keys per kv-head."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    padded: bool        # per-batch key lengths drawn from [Nk // 2, Nk]
+    std: float
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32))
+
+
+DECODE_WORKLOADS = {
+    # one new token per sequence against a 16k-key cache, with the grouped heads and key padding of
+    # the grouped-query forward workload (c4)
+    "decode": DecodeWorkload("decode", 4, 32, 8, 1, 16384, 128, True, 1.0, 6),
+}
+
+
+def make_decode(w: DecodeWorkload) -> dict:
+    """Same recipe as ``make``: Q [B,Hq,Nq,d], then K, V [B,Hkv,Nk,d] (bf16), then key lengths
+    uniform in [Nk // 2, Nk] when padded."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed)
+
+    def draw(*shape):
+        return (torch.randn(*shape, generator=g, dtype=torch.float32) * w.std).to(torch.bfloat16)
+
+    out = {"q": draw(w.B, w.Hq, w.Nq, w.d), "k": draw(w.B, w.Hkv, w.Nk, w.d),
+           "v": draw(w.B, w.Hkv, w.Nk, w.d), "key_lens": None, "scale": w.scale}
+    if w.padded:
+        out["key_lens"] = torch.randint(w.Nk // 2, w.Nk + 1, (w.B,), generator=g,
+                                        dtype=torch.int32)
+    return out
+
+
 def worked_example() -> dict:
     """The tutorial page's worked example (N = 4, d = 2): Q = K, V as printed, scale 1/sqrt(2)."""
     q = torch.tensor([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0], [0.0, 0.0]])

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum {
     FA_OK = 0,
@@ -128,6 +128,32 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
                     const int32_t* key_lens, float* dq, const void* workspace,
                     size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, float scale,
                     int causal, fa_dtype dtype, void* stream);
+
+/*
+ * Split-KV forward for decode shapes: Nq query rows per q-head (typically a few) against Nk
+ * cached keys (guide page "FlashAttention", Key takeaways: decode wants a different mapping of
+ * the same math).  Every query row of batch b sees keys [0, key_lens[b]) (Nk if key_lens is
+ * NULL); there is no causal mask.  The keys are cut into ranges, each range's partial output and
+ * log-sum-exp go to the workspace, and a second kernel merges them with the tutorial's step-3
+ * identity (page "Flash attention and efficient attention", Derivation: Incremental Softmax).
+ *   q, o : [B][Hq][Nq][d] bf16        k, v : [B][Hkv][Nk][d] bf16
+ *   lse  : [B][Hq][Nq] fp32 natural log, or NULL
+ *   num_splits: number of key ranges, 0 = let the library choose (fa_fwd_splitkv_splits)
+ *   workspace: device memory of at least fa_fwd_splitkv_workspace_size() bytes, contents ignored
+ * Only FA_BF16 with d in {64, 128}.  Same alignment, error and ordering rules as fa_fwd.
+ */
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const int32_t* key_lens, void* workspace, size_t workspace_bytes, int B,
+                         int Hq, int Hkv, int Nq, int Nk, int d, float scale, int num_splits,
+                         fa_dtype dtype, void* stream);
+
+/* Number of key ranges fa_fwd_splitkv uses for these arguments (num_splits = 0 lets the library
+ * choose); 0 for an invalid shape. */
+int fa_fwd_splitkv_splits(int B, int Hq, int Hkv, int Nq, int Nk, int num_splits);
+
+/* Bytes of workspace fa_fwd_splitkv needs: splits * B * Hq * Nq * (d + 1) fp32; 0 for an invalid
+ * shape. */
+size_t fa_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
 
 /* Name of the kernel instance fa_fwd / fa_bwd_dkdv / fa_bwd_dq would launch for these arguments
  * ("none" if unsupported); a static string, never freed. */

@@ -29,7 +29,8 @@ def lib():
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq",
-            "fa_bwd_workspace_size", "fa_status_str", "fa_abi_version"} <= set(names)
+            "fa_bwd_workspace_size", "fa_status_str", "fa_abi_version", "fa_fwd_splitkv",
+            "fa_fwd_splitkv_splits", "fa_fwd_splitkv_workspace_size"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -126,6 +127,38 @@ def test_bwd_stage_argument_errors(lib):
                          1, fa.FA_BF16, None) == SCALE
 
 
+def skv(lib, q=A, k=A, v=A, o=A, lse=A, kl=None, ws=A, wsb=1 << 24, B=2, Hq=8, Hkv=2, Nq=1,
+        Nk=1000, d=128, scale=0.1, splits=0, dtype=fa.FA_BF16):
+    return lib.fa_fwd_splitkv(q, k, v, o, lse, kl, ws, wsb, B, Hq, Hkv, Nq, Nk, d,
+                              ctypes.c_float(scale), splits, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=fa.FA_F32), DTYPE), (dict(dtype=5), DTYPE), (dict(d=96), HEADDIM),
+    (dict(Hq=6, Hkv=4), GQA), (dict(Hkv=0), SHAPE), (dict(Nq=-1), SHAPE), (dict(Nk=-3), SHAPE),
+    (dict(splits=-1), SHAPE), (dict(scale=float("nan")), SCALE),
+    (dict(q=None), NULL), (dict(o=None), NULL), (dict(k=None), NULL),
+    (dict(ws=None), WORKSPACE), (dict(wsb=100), WORKSPACE),
+    (dict(v=A + 8), ALIGN), (dict(ws=A + 4), ALIGN), (dict(lse=A + 1), ALIGN),
+    (dict(B=0, q=None, ws=None), OK), (dict(Nq=0, ws=None), OK),
+])
+def test_splitkv_argument_errors_before_any_hip_call(lib, kw, code):
+    assert skv(lib, **kw) == code
+
+
+def test_splitkv_plan_and_workspace(lib):
+    # automatic: enough ranges for ~1024 workgroups, each a multiple of 128 keys
+    assert fa.fa_fwd_splitkv_splits(4, 32, 8, 1, 16384) == 32
+    assert fa.fa_fwd_splitkv_splits(1, 1, 1, 1, 100) == 1
+    assert fa.fa_fwd_splitkv_splits(1, 1, 1, 1, 0) == 1
+    assert fa.fa_fwd_splitkv_splits(2, 16, 16, 4, 4096, 3) == 3        # requested
+    assert fa.fa_fwd_splitkv_splits(2, 16, 16, 4, 300, 50) == 3        # capped at ceil(Nk/128)
+    s = fa.fa_fwd_splitkv_splits(4, 32, 8, 1, 16384)
+    assert fa.fa_fwd_splitkv_workspace_size(4, 32, 8, 1, 16384, 128) == s * 4 * 32 * 1 * 129 * 4
+    assert fa.fa_fwd_splitkv_workspace_size(4, 32, 8, 1, 16384, 128, -1) == 0
+    assert fa.fa_fwd_splitkv_splits(4, 30, 8, 1, 16384) == 0           # Hq % Hkv != 0
+
+
 def _gpu_present():
     import torch
     return torch.cuda.is_available()
@@ -135,4 +168,5 @@ def _gpu_present():
 def test_valid_call_without_device_reports_device_error(lib):
     assert fwd(lib) == DEVICE
     assert bwd(lib) == DEVICE
+    assert skv(lib) == DEVICE
     assert fwd(lib, B=0) == OK              # empty problems never touch HIP at all
