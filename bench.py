@@ -2,6 +2,7 @@
 """Bench: exact tiled attention forward + backward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu-baseline]
+    python bench.py --workload decode     (split-KV decode forward, GB/s against the HBM roofline)
 
 One step = one pass of the whole hot path over one batch of synthetic inputs already resident
 in HBM: fa_fwd (O and LSE) then fa_bwd (its stages fa_bwd_prep, fa_bwd_dkdv, fa_bwd_dq), bf16 with
@@ -36,10 +37,13 @@ KERNEL_SRC = {                 # kernel -> sources whose hash guards stored coun
     "bwd_prep": [_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_device.h"],
     "bwd_dkdv": [_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_device.h"],
     "bwd_dq": [_CSRC + "fa_bwd_dq.hip", _CSRC + "fa_device.h"],
+    "splitkv": [_CSRC + "fa_splitkv.hip", _CSRC + "fa_device.h"],
+    "splitkv_merge": [_CSRC + "fa_splitkv.hip", _CSRC + "fa_device.h"],
 }
 # rocprofv3 kernel-name fragment -> kernel key
 KERNEL_MATCH = [("bwd_prep", "bwd_prep"), ("bwd_dkdv", "bwd_dkdv"), ("bwd_dq", "bwd_dq"),
-                ("fwd_bf16", "fwd_bf16")]
+                ("fwd_bf16", "fwd_bf16"), ("splitkv_merge", "splitkv_merge"),
+                ("splitkv_bf16", "splitkv")]
 COPY_CALIB_BYTES = 1 << 30
 
 
@@ -83,6 +87,17 @@ def bwd_kernel_bytes_compulsory(B, Hq, Hkv, N, d, elem=2):
     return {"bwd_prep": 2 * q + rows + 2 * rows,
             "bwd_dkdv": 2 * q + 2 * kv + 2 * rows + 2 * B * Hkv * N * d * 4,
             "bwd_dq": 2 * q + 2 * kv + 2 * rows + B * Hq * N * d * 4}
+
+
+def decode_kernel_bytes_compulsory(w, key_lens, splits, elem=2):
+    """Decode (split-KV): the range kernel reads the valid K and V rows once and Q, and writes
+    each range's fp32 partial output and LSE; the merge reads those and writes O and LSE."""
+    L = [w.Nk] * w.B if key_lens is None else [int(x) for x in key_lens.tolist()]
+    kv = sum(2 * w.Hkv * l * w.d * elem for l in L)
+    rows = w.B * w.Hq * w.Nq
+    part = splits * rows * (w.d + 1) * 4
+    return {"splitkv": kv + rows * w.d * elem + part,
+            "splitkv_merge": part + rows * w.d * elem + rows * 4}
 
 
 def naive_bytes(B, Hq, N, elem=2):
@@ -152,11 +167,30 @@ def traffic_summary(d, workload, cmd_note):
     fr = kib / f["copy_FETCH_SIZE"]["copy"]
     fw = kib / f["copy_WRITE_SIZE"]["copy"]
     import fa_inputs as fi
-    w = fi.WORKLOADS[workload]
-    comp = {"fwd_bf16": fwd_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d),
-            **bwd_kernel_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d)}
+    if workload in fi.DECODE_WORKLOADS:
+        w = fi.DECODE_WORKLOADS[workload]
+        x = fi.make_decode(w)
+        import exact_io_aware_68_amd as fa
+        splits = fa.fa_fwd_splitkv_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, 0)
+        comp = decode_kernel_bytes_compulsory(w, x["key_lens"], splits)
+        kernels = ("splitkv", "splitkv_merge")
+        title = (f"B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} d={w.d} bf16, key lengths "
+                 f"U[Nk/2, Nk], {splits} key ranges")
+        comp_note = ("Compulsory bytes: the range kernel reads the valid K and V rows once and Q "
+                     "and writes each range's fp32 partial output and LSE; the merge reads those "
+                     "and writes O and LSE.")
+    else:
+        w = fi.WORKLOADS[workload]
+        comp = {"fwd_bf16": fwd_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d),
+                **bwd_kernel_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d)}
+        kernels = ("fwd_bf16", "bwd_prep", "bwd_dkdv", "bwd_dq")
+        title = f"B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} causal={w.causal} {w.dtype}"
+        comp_note = ("`vs compulsory` divides by the tiled IO count (read Q, K, V once, write O "
+                     "and LSE once).  Compulsory bytes of the backward kernels: prep reads O, dO, "
+                     "LSE and writes D and the base-2 LSE; dK/dV reads Q, dO, K, V and both row "
+                     "statistics and writes fp32 dK, dV; dQ reads the same and writes fp32 dQ.")
     rows = []
-    for k in ("fwd_bf16", "bwd_prep", "bwd_dkdv", "bwd_dq"):
+    for k in kernels:
         if k not in f["bench_FETCH_SIZE"]:
             continue
         rd, wr = f["bench_FETCH_SIZE"][k], f["bench_WRITE_SIZE"][k]
@@ -165,8 +199,7 @@ def traffic_summary(d, workload, cmd_note):
         rows.append(f"| {k} | {_src_hash(KERNEL_SRC[k])} | {rd:.0f} | {wr:.0f} | "
                     f"{(rd * fr + wr * fw) / 1024:.1f} | {byt} | "
                     f"{'-' if c is None else f'{byt / c:.3f}'} |")
-    txt = f"""# HBM traffic per launch — workload {workload}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} \
-d={w.d} causal={w.causal} {w.dtype}
+    txt = f"""# HBM traffic per launch — workload {workload}: {title}
 
 Counters from four `rocprofv3 --pmc` runs (one counter each), averaged over the dispatches of
 each kernel:
@@ -176,11 +209,9 @@ each kernel:
 Calibration: a plain device copy of {COPY_CALIB_BYTES} bytes (`bench.py --copy-calib`) reads
 FETCH_SIZE = {f['copy_FETCH_SIZE']['copy']:.0f} KiB and WRITE_SIZE =
 {f['copy_WRITE_SIZE']['copy']:.0f} KiB per dispatch, so FETCH_SIZE is scaled by {fr:.3f} and
-WRITE_SIZE by {fw:.3f}.  `bytes/launch` = calibrated FETCH + WRITE; `vs compulsory` divides by
-the tiled IO count (read Q, K, V once, write O and LSE once).  `src` is the hash bench.py
-compares with the kernel's current sources: a stale row reads as unmeasured.  Compulsory bytes
-of the backward kernels: prep reads O, dO, LSE and writes D and the base-2 LSE; dK/dV reads Q,
-dO, K, V and both row statistics and writes fp32 dK, dV; dQ reads the same and writes fp32 dQ.
+WRITE_SIZE by {fw:.3f}.  `bytes/launch` = calibrated FETCH + WRITE.  `src` is the hash
+bench.py compares with the kernel's current sources: a stale row reads as unmeasured.
+{comp_note}
 
 | kernel | src | FETCH_SIZE KiB | WRITE_SIZE KiB | calibrated MiB | bytes/launch | vs compulsory |
 |---|---|---|---|---|---|---|
@@ -244,6 +275,89 @@ TRAFFIC_CMD = """    cd /tmp && export TMPDIR=/tmp
     done
     python3 $REPO/bench.py --traffic-summary $REPO/gpurun_out/pmc"""
 
+def bench_decode(args):
+    """Split-KV decode forward on a decode workload: one step = one fa_fwd_splitkv call (the range
+    kernel and the merge kernel) with inputs resident in HBM.  Bound by HBM: reports GB/s of the
+    algorithmic bytes against the 8 TB/s peak."""
+    import torch
+
+    import exact_io_aware_68_amd as fa
+    import fa_inputs as fi
+    w = fi.DECODE_WORKLOADS[args.workload]
+    x = fi.make_decode(w)
+    dev = "cuda:0"
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    kl = None if x["key_lens"] is None else x["key_lens"].to(dev)
+    splits = fa.fa_fwd_splitkv_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, args.splits)
+    ws = torch.empty(fa.fa_fwd_splitkv_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, splits),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    # The K/V cache (185 MB here) would fit the 256 MB Infinity Cache; a decode step in service
+    # reads it cold, so a 512 MiB buffer is READ before every timed call (outside the events):
+    # reading evicts the caches without leaving dirty lines whose write-back would compete with
+    # the timed reads.
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def call():
+        fa.fa_fwd_splitkv(q, k, v, scale=x["scale"], key_lens=kl, num_splits=splits, o=o, lse=lse,
+                          workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        torch.sum(flush, dim=0, out=sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    comp = decode_kernel_bytes_compulsory(w, x["key_lens"], splits)
+    byt = comp["splitkv"] + comp["splitkv_merge"]
+    gbs = byt / (ms * 1e-3) / 1e9
+    meas = [stored_traffic(n, args.workload) for n in ("splitkv", "splitkv_merge")]
+    out = {
+        "metric": "split-KV decode attention GB/s (algorithmic bytes), HBM roofline",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "wall_ms_per_step_with_cache_flush": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"split-KV decode B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} "
+                               f"Nk={w.Nk} d={w.d} key_lens=U[Nk/2,Nk] splits={splits}",
+                   "seed": w.seed, "parallelism": "single GPU"},
+        "kernels_ms": {"splitkv+merge": round(ms, 4)},
+        "algorithmic_bytes": byt,
+        "roofline": {"kernel": "splitkv+merge", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None if None in meas else sum(meas)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import attn_decode
+        t1 = time.perf_counter()
+        attn_decode(x["q"], x["k"], x["v"], x["scale"], x["key_lens"])
+        dt = time.perf_counter() - t1
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        out["cpu_baseline"] = {"value": round(byt / dt / 1e9, 3), "unit": "GB/s",
+                               "cores": int(threads), "kind": "oracle",
+                               "sample": f"fp64 numpy oracle over the whole workload in {dt:.2f} s "
+                                         f"(same byte count); host affinity "
+                                         f"{len(os.sched_getaffinity(0))} cpus"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,12 +366,19 @@ def main():
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--only", choices=["fwd", "bwd", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="decode workloads: number of key ranges (0: the library's choice)")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--traffic-summary", metavar="DIR",
                     help="write profiles/hbm_traffic_<workload>.md from rocprofv3 --pmc CSVs")
     args = ap.parse_args()
     if args.traffic_summary:
-        traffic_summary(args.traffic_summary, args.workload, TRAFFIC_CMD)
+        cmd = TRAFFIC_CMD
+        if args.workload != "c3":
+            cmd = (cmd.replace("bench.py --steps", f"bench.py --workload {args.workload} --steps")
+                      .replace("--traffic-summary", f"--workload {args.workload} --traffic-summary")
+                      .replace("gpurun_out/pmc", "gpurun_out/pmcd"))
+        traffic_summary(args.traffic_summary, args.workload, cmd)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the attention path is "
@@ -265,6 +386,10 @@ def main():
         sys.exit(2)
     if args.copy_calib:
         copy_calibration()
+        return
+    import fa_inputs as fi
+    if args.workload in fi.DECODE_WORKLOADS:
+        bench_decode(args)
         return
 
     import torch

@@ -250,7 +250,7 @@ static fa_status check_splitkv_shape(int B, int Hq, int Hkv, int Nq, int Nk, int
     splitkv_plan(B, Hq, Hkv, Nq, Nk, num_splits, &splits, &kps);
     const long double rows = (long double)(Hq / Hkv) * Nq;
     if ((long double)B * Hkv * ((rows + 31) / 32 + 1) * splits > 4.0e9L) return FA_ERR_SHAPE;
-    if ((long double)B * Hq * Nq * (d / 8 + 1) > 4.0e9L * 256) return FA_ERR_SHAPE;
+    if ((long double)B * Hq * Nq > 4.0e9L) return FA_ERR_SHAPE;   // merge: one workgroup per row
     return FA_OK;
 }
 

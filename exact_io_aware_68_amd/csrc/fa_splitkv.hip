@@ -14,10 +14,12 @@
 //     The kernel is bound by HBM (every K and V byte is read once), not by the MFMA.
 //   * 4 waves per workgroup split the range's 32-key steps round-robin; each wave carries its own
 //     online-softmax state and the four are merged through LDS at the end.
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 takes its K operands straight from global memory
-//     (each lane loads the 16-byte chunks of its key row it needs; no LDS).  V rows are loaded
-//     into registers one step ahead, stored into the wave's own swizzled LDS tile and read back
-//     transposed (ds_read_b64_tr_b16) as the A operand of O^T += V^T P^T.
+//   * K and V rows are loaded with whole rows per 16 lanes (fully used cache lines), one step
+//     ahead, into registers, then stored into the wave's own swizzled LDS tiles: K is read back
+//     by rows as the A operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), V transposed
+//     (ds_read_b64_tr_b16) as the A operand of O^T += V^T P^T.  (Loading each lane's own K-row
+//     chunks straight into operand registers touches 32 rows per instruction in 32-byte pieces,
+//     which measured far slower from HBM.)
 //   * Keys at or beyond key_lens[b] arrive as zeros through the buffer bound and are masked.
 //   * Reference point of the exponentials: the row max of each wave's first step, moved only
 //     when a step's exponentials would sum past 2^16 (as in the forward).
@@ -43,8 +45,11 @@ struct CombineLds {
 
 template <int D>
 union SplitLds {
-    bf16 v[kWaves][kBC * D];   // one swizzled V tile per wave
-    CombineLds<D> c;           // reused after the key loop
+    struct {
+        bf16 k[kWaves][kBC * D];   // one swizzled K tile per wave
+        bf16 v[kWaves][kBC * D];   // one swizzled V tile per wave
+    } t;
+    CombineLds<D> c;               // reused after the key loop
 };
 
 }  // namespace
@@ -104,42 +109,47 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_bf16_kernel(SplitParams p
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
         for (int xx = 0; xx < 2; ++xx) tro[dt][xx] = tr_swz_offset<D>(lane, 32 * dt, xx);
-    bf16* const Vs = sm.v[w];
+    bf16* const Ks = sm.t.k[w];
+    bf16* const Vs = sm.t.v[w];
+    // Row reads of K: row c, chunk 2s + hh.
+    int kro[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kro[s] = swz_at<D>(c, 16 * s + 8 * hh);
 
-    // Loads of step t (keys ks + 32 t ..): the lane's K row chunks (A operands of S^T) and V
-    // chunks (contiguous mapping); rows >= Lk arrive as zeros.  The row counts are uniform per
-    // wave; readfirstlane keeps the resources in scalar registers.
-    auto load = [&](int t, bf16x8 (&kf)[NS], u32x4 (&vr)[VCH]) {
+    // Loads of step t (keys ks + 32 t ..), K and V chunks in the contiguous mapping (chunk id =
+    // lane + 64 i: row id / CPR, columns 8 (id % CPR)); rows >= Lk arrive as zeros.  The row
+    // counts are uniform per wave; readfirstlane keeps the resources in scalar registers.
+    auto load = [&](int t, u32x4 (&kr)[VCH], u32x4 (&vr)[VCH]) {
         const int k0 = ks + kBC * t;
         const uint32_t nb =
             (uint32_t)__builtin_amdgcn_readfirstlane(max(min(Lk - k0, kBC), 0)) * D * 2;
         const rsrc_t rk = make_rsrc(K + (size_t)k0 * D, nb);
         const rsrc_t rv = make_rsrc(V + (size_t)k0 * D, nb);
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-            kf[s] = __builtin_bit_cast(bf16x8, buf_ld16(rk, (c * D + 16 * s + 8 * hh) * 2));
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) vr[i] = buf_ld16(rv, (lane + 64 * i) * 16);
+        for (int i = 0; i < VCH; ++i) {
+            kr[i] = buf_ld16(rk, (lane + 64 * i) * 16);
+            vr[i] = buf_ld16(rv, (lane + 64 * i) * 16);
+        }
     };
 
-    bf16x8 kc[NS];
-    u32x4 vc[VCH];
+    u32x4 kc[VCH], vc[VCH];
     if (w < nsteps) load(w, kc, vc);
     for (int t = w; t < nsteps; t += kWaves) {
-        // V tile of step t into this wave's LDS tile (its previous contents were last read by
+        // Tiles of step t into this wave's LDS tiles (their previous contents were last read by
         // this wave's previous step, earlier in program order); then the loads of the wave's
-        // next step are issued into the same V registers, so they fly during this step.
+        // next step are issued into the same registers, so they fly during this step.
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
             const int id = lane + 64 * i;
-            st16(Vs + swz_at<D>(id / CPR, 8 * (id % CPR)), vc[i]);
+            const int off = swz_at<D>(id / CPR, 8 * (id % CPR));
+            st16(Ks + off, kc[i]);
+            st16(Vs + off, vc[i]);
         }
-        bf16x8 kn[NS];
-        const bool more = t + kWaves < nsteps;
-        if (more) load(t + kWaves, kn, vc);
+        if (t + kWaves < nsteps) load(t + kWaves, kc, vc);
         f32x16 st = f32x16{};
 #pragma unroll
-        for (int s = 0; s < NS; ++s) st = mfma32(kc[s], qf[s], st);
+        for (int s = 0; s < NS; ++s)
+            st = mfma32(__builtin_bit_cast(bf16x8, ld16(Ks + kro[s])), qf[s], st);
         const int k0 = ks + kBC * t;
         if (k0 + kBC > Lk) {   // C row rr -> key k0 + 8(rr/4) + 4hh + rr%4
 #pragma unroll
@@ -188,10 +198,6 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_bf16_kernel(SplitParams p
                 const bf16x8 vf = join(lds_tr(vb + tro[dt][0]), lds_tr(vb + tro[dt][1]));
                 oacc[dt] = mfma32(vf, pf[u], oacc[dt]);
             }
-        if (more) {
-#pragma unroll
-            for (int s = 0; s < NS; ++s) kc[s] = kn[s];
-        }
     }
 
     // ---- merge the four waves' states (same rows, disjoint keys) through LDS --------------
@@ -247,44 +253,64 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_bf16_kernel(SplitParams p
     }
 }
 
-// Merge of the key ranges' partial results: one thread per (row, 8 columns).
+// Merge of the key ranges' partial results: one workgroup per query row; thread t takes 8
+// columns (chunk t % (D/8)) of the ranges t / (D/8), t / (D/8) + SP, ...; the partial sums are
+// reduced through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitParams p) {
-    constexpr int CH = D / 8;
+    constexpr int CH = D / 8;          // 8-column chunks per row
+    constexpr int SP = 256 / CH;       // ranges taken in parallel
+    __shared__ float red_m[256];
+    __shared__ float red_l[SP];
+    __shared__ f32x4 red_o[SP][CH][2];
     const long long rows = (long long)p.B * p.Hq * p.Nq;
-    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (gid >= rows * CH) return;
-    const long long row = gid / CH;
-    const int ch = (int)(gid - row * CH);
+    const long long row = blockIdx.x;
+    const int t = threadIdx.x, ch = t % CH, s0 = t / CH;
+
     float M = kNegInf;
-    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.lpart[s * rows + row]);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = s0; s < p.splits; s += SP) M = fmaxf(M, p.lpart[s * rows + row]);
+    red_m[t] = M;
+    __syncthreads();
+    M = kNegInf;
+    for (int i = 0; i < 256; i += CH) M = fmaxf(M, red_m[i]);   // one entry per range group
+
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, bq = {0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
     if (M != kNegInf) {
-        for (int s = 0; s < p.splits; ++s) {
+        for (int s = s0; s < p.splits; s += SP) {
             const float wgt = exp2_hw((p.lpart[s * rows + row] - M) * kLog2e);   // 0 for -inf
             L += wgt;
             const f32x4* src = reinterpret_cast<const f32x4*>(p.opart + (s * rows + row) * D + 8 * ch);
-            const f32x4 a = src[0], bq = src[1];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[i] += wgt * a[i];
-                acc[4 + i] += wgt * bq[i];
-            }
+            a += wgt * src[0];
+            bq += wgt * src[1];
         }
     }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    bf16* o = (bf16*)p.o + row * D + 8 * ch;
-    *reinterpret_cast<bf16x8*>(o) = to_bf16x8(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv,
-                                              acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-    if (ch == 0 && p.lse) p.lse[row] = L > 0.f ? M + logf(L) : kNegInf;
+    red_o[s0][ch][0] = a;
+    red_o[s0][ch][1] = bq;
+    if (ch == 0) red_l[s0] = L;
+    __syncthreads();
+    if (t < CH) {
+        f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = {0.f, 0.f, 0.f, 0.f};
+        float Ls = 0.f;
+#pragma unroll 4
+        for (int i = 0; i < SP; ++i) {
+            oa += red_o[i][t][0];
+            ob += red_o[i][t][1];
+            Ls += red_l[i];
+        }
+        const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+        bf16* o = (bf16*)p.o + row * D + 8 * t;
+        *reinterpret_cast<bf16x8*>(o) = to_bf16x8(oa[0] * inv, oa[1] * inv, oa[2] * inv,
+                                                  oa[3] * inv, ob[0] * inv, ob[1] * inv,
+                                                  ob[2] * inv, ob[3] * inv);
+        if (t == 0 && p.lse) p.lse[row] = Ls > 0.f ? M + logf(Ls) : kNegInf;
+    }
 }
 
 hipError_t launch_splitkv_bf16(const SplitParams& p, hipStream_t stream) {
     const int G = p.Hq / p.Hkv, R = G * p.Nq, nrt = (R + kRows - 1) / kRows;
     dim3 grid1((unsigned)((long long)p.B * p.Hkv * nrt * p.splits)), block(kThreads);
-    const long long n2 = (long long)p.B * p.Hq * p.Nq * (p.d / 8);
-    dim3 grid2((unsigned)((n2 + 255) / 256)), block2(256);
+    dim3 grid2((unsigned)((long long)p.B * p.Hq * p.Nq)), block2(256);
     if (p.d == 128) {
         hipLaunchKernelGGL(splitkv_bf16_kernel<128>, grid1, block, 0, stream, p);
         hipLaunchKernelGGL(splitkv_merge_kernel<128>, grid2, block2, 0, stream, p);
