@@ -16,13 +16,16 @@ What it computes (sources are the three pages on FlashAttention):
   online/blocked form is NOT used here; ``oracle.blocked`` models it separately so that tests can
   compare the two.
 * Masks: the guide page ("Tiling through SRAM") lists causal masks, padding and grouped-query
-  attention as tiling details that leave the result definition unchanged.  Readings taken where
-  the pages are silent:
+  attention as tiling details that leave the result definition unchanged; the tutorial page adds
+  a local attention window ("Other Efficient Attention Variants").  Readings taken where the
+  pages are silent:
     - causal is top-left aligned: query i sees keys j <= i;
     - padding is a per-batch key length L_b: keys j >= L_b are invisible to every query of batch b,
       query rows are still computed;
     - grouped-query heads use contiguous groups: q-head h reads kv-head h * Hkv // Hq;
-    - a row with no visible key has O = 0 and LSE = -inf, and contributes no gradient.
+    - a row with no visible key has O = 0 and LSE = -inf, and contributes no gradient;
+    - a local window (left, right) lets row i see keys i - left .. i + right; the page's window
+      w (odd) is left = right = (w - 1) / 2.
 * Saved metadata (guide page, "Tiling through SRAM": a little softmax metadata is written in
   training): read as the natural-log log-sum-exp of each row's scaled, masked scores,
   LSE_i = m_i + ln(sum_j exp(s_ij - m_i)).
@@ -60,12 +63,24 @@ def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
     return (h * Hkv) // Hq
 
 
-def visible_mask(rows: np.ndarray, L: int, causal: bool) -> np.ndarray:
-    """Boolean [len(rows), L]: key j is visible to query row i iff j < L and (not causal or j <= i)."""
+def visible_mask(rows: np.ndarray, L: int, causal: bool, window=None) -> np.ndarray:
+    """Boolean [len(rows), L]: key j is visible to query row i iff j < L and (not causal or j <= i)
+    and, with window = (left, right), i - left <= j <= i + right (a negative side is unbounded).
+
+    The window is the tutorial page's local attention window ("Other Efficient Attention
+    Variants", worked example: w = 3 lets each token see itself and one neighbour on each side,
+    i.e. left = right = (w - 1) / 2)."""
     j = np.arange(L)[None, :]
+    i = np.asarray(rows)[:, None]
     vis = np.ones((len(rows), L), dtype=bool)
     if causal:
-        vis &= j <= np.asarray(rows)[:, None]
+        vis &= j <= i
+    if window is not None:
+        left, right = window
+        if left >= 0:
+            vis &= j >= i - left
+        if right >= 0:
+            vis &= j <= i + right
     return vis
 
 
@@ -101,13 +116,14 @@ def _softmax_rows(s: np.ndarray, vis: np.ndarray):
 
 
 def attn_fwd(q, k, v, scale: float, causal: bool = False, key_lens=None,
-             heads=None, chunk: int = 1024):
+             heads=None, chunk: int = 1024, window=None):
     """Exact attention forward.
 
     q: [B, Hq, N, d]; k, v: [B, Hkv, N, d] (any float type, widened to fp64).
     Returns (O [B, Hq, N, d] fp64, LSE [B, Hq, N] fp64, natural log).
     ``heads``: optional iterable of (b, h) pairs to compute; other entries stay O = 0, LSE = nan.
     ``chunk``: query rows per block; chunking over query rows does not change any row's math.
+    ``window``: optional (left, right) local window, see ``visible_mask``.
     """
     q, k, v = to64(q), to64(k), to64(v)
     B, Hq, N, d = q.shape
@@ -125,7 +141,7 @@ def attn_fwd(q, k, v, scale: float, causal: bool = False, key_lens=None,
         for r0 in range(0, N, chunk):
             rows = np.arange(r0, min(N, r0 + chunk))
             s = score_rows(q[b, h, rows], K, scale)
-            P, m, l = _softmax_rows(s, visible_mask(rows, L, causal))
+            P, m, l = _softmax_rows(s, visible_mask(rows, L, causal, window))
             O[b, h, rows] = P @ V
             with np.errstate(divide="ignore"):
                 LSE[b, h, rows] = np.where(np.isfinite(m), m + np.log(np.where(l > 0, l, 1.0)),
@@ -164,7 +180,7 @@ def attn_decode(q, k, v, scale: float, key_lens=None):
     return O, LSE
 
 
-def attn_fwd_rows(q, k, v, scale: float, causal: bool, key_lens, picks):
+def attn_fwd_rows(q, k, v, scale: float, causal: bool, key_lens, picks, window=None):
     """Forward for individual rows: ``picks`` is a list of (b, h, i).
 
     Returns (O_rows [len(picks), d], LSE_rows [len(picks)]).  Each row is computed on its own from
@@ -184,7 +200,7 @@ def attn_fwd_rows(q, k, v, scale: float, causal: bool, key_lens, picks):
             cache[(b, g)] = (to64(k[b, g, :L]), to64(v[b, g, :L]))
         K, V = cache[(b, g)]
         s = score_rows(to64(q[b, h, i:i + 1]), K, scale)
-        P, m, l = _softmax_rows(s, visible_mask(np.array([i]), L, causal))
+        P, m, l = _softmax_rows(s, visible_mask(np.array([i]), L, causal, window))
         O[n] = (P @ V)[0]
         LSE[n] = m[0] + np.log(l[0]) if np.isfinite(m[0]) else -np.inf
     return O, LSE
