@@ -14,6 +14,7 @@ The functions carry the C names (see include/fa.h for the full contract):
     fa_bwd_workspace_size, fa_fwd_kernel_name, fa_bwd_dkdv_kernel_name, fa_bwd_dq_kernel_name,
     fa_status_str, fa_abi_version
     fa_fwd_splitkv(q, k, v, *, scale, key_lens, num_splits, o, lse)  -> (o, lse)   (decode shapes)
+    fa_fwd_window(q, k, v, *, window, scale, key_lens, o, lse)       -> (o, lse)   (local window)
     fa_fwd_splitkv_splits, fa_fwd_splitkv_workspace_size
 
 Tensors are [B, H, N, d] contiguous ("BHND"); q/k/v/o/dO are bf16 (d in {64, 128}) or fp32
@@ -30,7 +31,7 @@ __all__ = [
     "FAError", "lib_path", "load", "fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq",
     "fa_bwd_workspace_size", "fa_fwd_kernel_name", "fa_bwd_dkdv_kernel_name",
     "fa_bwd_dq_kernel_name", "fa_status_str", "fa_abi_version", "FA_F32", "FA_BF16",
-    "fa_fwd_splitkv", "fa_fwd_splitkv_splits", "fa_fwd_splitkv_workspace_size",
+    "fa_fwd_splitkv", "fa_fwd_splitkv_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_window",
 ]
 
 FA_F32, FA_BF16 = 0, 1
@@ -70,6 +71,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_dq.restype = I
     lib.fa_bwd_workspace_size.argtypes = [I, I, I, I]
     lib.fa_bwd_workspace_size.restype = Z
+    lib.fa_fwd_window.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, I, I, P]
+    lib.fa_fwd_window.restype = I
     lib.fa_fwd_splitkv.argtypes = [P, P, P, P, P, P, P, Z, I, I, I, I, I, I, F, I, I, P]
     lib.fa_fwd_splitkv.restype = I
     lib.fa_fwd_splitkv_splits.argtypes = [I, I, I, I, I, I]
@@ -174,6 +177,30 @@ def fa_fwd(q, k, v, *, scale: float | None = None, causal: bool = False, key_len
                        Hkv, N, d, ctypes.c_float(_default_scale(d) if scale is None else scale),
                        int(causal), _dtype_code(q), _stream(stream, q.device))
     _check("fa_fwd", st)
+    return o, lse
+
+
+def fa_fwd_window(q, k, v, *, window, scale: float | None = None, key_lens=None, o=None,
+                  lse=None, want_lse: bool = True, stream=None):
+    """Forward with a local window (left, right): row i sees keys i - left .. i + right (a
+    negative side is unbounded).  Returns (o, lse)."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shape(q, k)
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if key_lens is not None and key_lens.dtype != torch.int32:
+        raise ValueError("key_lens must be int32")
+    left, right = window
+    st = load().fa_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(key_lens), B,
+                              Hq, Hkv, N, d,
+                              ctypes.c_float(_default_scale(d) if scale is None else scale),
+                              int(left), int(right), _dtype_code(q), _stream(stream, q.device))
+    _check("fa_fwd_window", st)
     return o, lse
 
 

@@ -48,6 +48,7 @@ constexpr int kNT = kBC / 32;   // 32-key blocks per compute step
 constexpr int kLT = 64;         // keys per LDS tile (two compute steps per barrier)
 constexpr int kThreads = 256;
 constexpr float kSumCap = 65536.f;   // largest partial sum of P before m moves
+constexpr int kWindowWavesPerSimd = 1;   // window instances: one wave per SIMD (no spills)
 
 template <bool B>
 struct Flag {
@@ -67,8 +68,12 @@ struct FwdLds {
 template <int NH>
 constexpr int rows_per_block() { return kWaves * 32 * NH; }
 
-template <int D, bool CAUSAL, int NH>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
+// WIN: local-window instance (tutorial page, "Other Efficient Attention Variants", Local
+// Attention Window): row i sees keys i - wl .. i + wr; the workgroup visits only the key tiles
+// its rows' windows overlap (O(N w) work), and masks per step where a window edge or the key
+// length cuts a step.
+template <int D, bool CAUSAL, int NH, bool WIN>
+__device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
     constexpr int kBR = rows_per_block<NH>();
     constexpr int kWR = 32 * NH;
     constexpr int NS = D / 16;      // reduction steps of Q K^T
@@ -95,6 +100,16 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
 
     int Lk = N;
     if (p.key_lens) Lk = min(max(p.key_lens[b], 0), N);
+    // First key the workgroup visits (a multiple of the LDS tile, so tile pairs stay aligned);
+    // 0 unless a left window edge lies beyond the first tile.  K and V below are rebased there,
+    // so every key index in the loop is relative to kb and Lr = Lk - kb.
+    int wl = -1, wr = -1, kb = 0;
+    if constexpr (WIN) {
+        wl = p.wl;
+        wr = p.wr;
+        if (wl >= 0) kb = (max(qt * kBR - wl, 0) / kLT) * kLT;
+    }
+    const int Lr = Lk - kb;
 
     const int q0 = qt * kBR + kWR * w;    // this wave's first query row; half h: q0 + 32h + c
     const float C = p.scale * kLog2e;
@@ -114,6 +129,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
 
     int kend = Lk;
     if (CAUSAL) kend = min(kend, qt * kBR + kBR);
+    if constexpr (WIN) {
+        if (wr >= 0) kend = min(kend, qt * kBR + kBR + wr);
+    }
+    kend = max(kend - kb, 0);                    // relative to kb from here on
     const int ntiles = (kend + kBC - 1) / kBC;
 
     f32x16 oacc[NH][ND];
@@ -155,12 +174,15 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
                 for (int h = 0; h < NH; ++h) st[h][t] = mfma32(kf, qf[h][s], st[h][t]);
             }
     };
-    auto need_mask = [&](int j) {
-        const int k0 = j * kBC;
-        return (CAUSAL && k0 + kBC - 1 > q0) || (k0 + kBC > Lk);
+    auto need_mask = [&](int j) {   // some key of step j hidden from some row of the wave
+        const int k0 = kb + j * kBC;
+        bool cut = (CAUSAL && k0 + kBC - 1 > q0) || (k0 + kBC > Lk);
+        if constexpr (WIN)
+            cut = cut || (wr >= 0 && k0 + kBC - 1 > q0 + wr) || (wl >= 0 && k0 < q0 + kWR - 1 - wl);
+        return cut;
     };
     auto mask = [&](int j, f32x16 (&st)[NH][kNT]) {
-        const int k0 = j * kBC;
+        const int k0 = kb + j * kBC;
 #pragma unroll
         for (int h = 0; h < NH; ++h)
 #pragma unroll
@@ -168,7 +190,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    const bool hide = key >= Lk || (CAUSAL && key > q0 + 32 * h + c);
+                    const int row = q0 + 32 * h + c;
+                    bool hide = key >= Lk || (CAUSAL && key > row);
+                    if constexpr (WIN)
+                        hide = hide || (wr >= 0 && key > row + wr) || (wl >= 0 && key < row - wl);
                     st[h][t][r] = hide ? kNegInf : st[h][t][r];
                 }
     };
@@ -248,18 +273,20 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
     auto vsub = [&](int j) { return sm.v[(j >> 1) & 1] + (j & 1) * kBC * D; };
     const int nlt = (kend + kLT - 1) / kLT;                       // V tiles
     const int nkt = kend > kBC ? (kend - kBC + kLT - 1) / kLT : 0;  // shifted K tiles
-    auto load_k = [&](int T) {   // shifted K tile T: keys 64 T + 32 .. 64 T + 95
+    const bf16* __restrict__ Kr = K + (size_t)kb * D;
+    const bf16* __restrict__ Vr = V + (size_t)kb * D;
+    auto load_k = [&](int T) {   // shifted K tile T: keys kb + 64 T + 32 .. kb + 64 T + 95
         const int k0 = T * kLT + kBC;
-        dma_tile<D, kLT, kWaves>(K + (size_t)k0 * D, Lk - k0, sm.k[T & 1], w, lane);
+        dma_tile<D, kLT, kWaves>(Kr + (size_t)k0 * D, Lr - k0, sm.k[T & 1], w, lane);
     };
     auto load_v = [&](int T) {
         const int k0 = T * kLT;
-        dma_tile<D, kLT, kWaves>(V + (size_t)k0 * D, Lk - k0, sm.v[T & 1], w, lane);
+        dma_tile<D, kLT, kWaves>(Vr + (size_t)k0 * D, Lr - k0, sm.v[T & 1], w, lane);
     };
     f32x16 sa[NH][kNT], sb[NH][kNT];
     bf16x8 pf[NH][kNT][2];
     if (ntiles > 0) {
-        dma_tile<D, kBC, kWaves>(K, Lk, sm.k[1] + kBC * D, w, lane);   // keys 0..31
+        dma_tile<D, kBC, kWaves>(Kr, Lr, sm.k[1] + kBC * D, w, lane);   // keys kb .. kb + 31
         load_v(0);
         if (nkt > 0) load_k(0);
     }
@@ -268,8 +295,9 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
     if (ntiles > 0) {
         scores(ksub(0), sa);
         if (need_mask(0)) mask(0, sa);
-        // The reference point starts at the row max of the first step (finite for every row:
-        // key 0 is valid for all of them when Lk >= 1).
+        // The reference point starts at the row max of the first step, or at 0 for a row that
+        // sees no key of it (possible with a window or a short key length): it is a reference
+        // point, never -inf, so every later rescale is a finite factor.
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
             float mx = kNegInf;
@@ -277,7 +305,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
             for (int t = 0; t < kNT; ++t)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[h][t][r]);
-            m[h] = max_with_partner(mx) * C;
+            mx = max_with_partner(mx) * C;
+            m[h] = mx == kNegInf ? 0.f : mx;
         }
     }
     __syncthreads();   // keys 0..31 in buffer 1 are overwritten by K tile 1 during steps 0, 1
@@ -298,17 +327,31 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
             __syncthreads();   // tiles T+1 visible; buffers T&1 free
         }
     };
-    // Steps below jfree need no mask for any row of the workgroup.
-    int jfree = Lk / kBC;
-    if (CAUSAL) jfree = min(jfree, (qt * kBR + 1) / kBC);
     int j = 0;   // stays even: pairs of steps share one LDS tile
-    for (; j + 2 < ntiles && j + 2 < jfree; j += 2) {
-        step(Flag<false>{}, Flag<false>{}, j, sa, sb);
-        step(Flag<false>{}, Flag<true>{}, j + 1, sb, sa);
-    }
-    for (; j + 2 < ntiles; j += 2) {
-        step(Flag<true>{}, Flag<false>{}, j, sa, sb);
-        step(Flag<true>{}, Flag<true>{}, j + 1, sb, sa);
+    if constexpr (WIN) {
+        // Window edges cut steps at both ends of the range: decide per pair of steps (the
+        // masks of S(j+1), S(j+2) belong to steps j, j+1).
+        for (; j + 2 < ntiles; j += 2) {
+            if (need_mask(j + 1) || need_mask(j + 2)) {
+                step(Flag<true>{}, Flag<false>{}, j, sa, sb);
+                step(Flag<true>{}, Flag<true>{}, j + 1, sb, sa);
+            } else {
+                step(Flag<false>{}, Flag<false>{}, j, sa, sb);
+                step(Flag<false>{}, Flag<true>{}, j + 1, sb, sa);
+            }
+        }
+    } else {
+        // Steps below jfree need no mask for any row of the workgroup.
+        int jfree = Lk / kBC;
+        if (CAUSAL) jfree = min(jfree, (qt * kBR + 1) / kBC);
+        for (; j + 2 < ntiles && j + 2 < jfree; j += 2) {
+            step(Flag<false>{}, Flag<false>{}, j, sa, sb);
+            step(Flag<false>{}, Flag<true>{}, j + 1, sb, sa);
+        }
+        for (; j + 2 < ntiles; j += 2) {
+            step(Flag<true>{}, Flag<false>{}, j, sa, sb);
+            step(Flag<true>{}, Flag<true>{}, j + 1, sb, sa);
+        }
     }
     if (j + 1 < ntiles) {
         step(Flag<true>{}, Flag<false>{}, j, sa, sb);   // no loads left: nothing issued
@@ -343,6 +386,16 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
     }
 }
 
+template <int D, bool CAUSAL, int NH>
+__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p) {
+    fwd_bf16_body<D, CAUSAL, NH, false>(p);
+}
+
+template <int D, int NH>
+__global__ __launch_bounds__(kThreads, kWindowWavesPerSimd) void fwd_window_bf16_kernel(FwdParams p) {
+    fwd_bf16_body<D, false, NH, true>(p);
+}
+
 // Halves per wave of the built instances.
 constexpr int kNH = 1;
 
@@ -361,6 +414,18 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
         else
             hipLaunchKernelGGL((fwd_bf16_kernel<64, false, kNH>), grid, block, 0, stream, p);
     }
+    return hipGetLastError();
+}
+
+// Local-window instances (a causal window is wr = 0).
+hipError_t launch_fwd_window_bf16(const FwdParams& p, hipStream_t stream) {
+    constexpr int kBR = rows_per_block<kNH>();
+    const int nqt = (p.N + kBR - 1) / kBR;
+    dim3 grid((unsigned)(nqt * p.Hq * p.B)), block(kThreads);
+    if (p.d == 128)
+        hipLaunchKernelGGL((fwd_window_bf16_kernel<128, kNH>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((fwd_window_bf16_kernel<64, kNH>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ struct FwdParams {
     int B, Hq, Hkv, N, d;
     float scale;
     int causal;
+    int wl = -1, wr = -1;     // local window: row i sees keys i - wl .. i + wr (-1: unbounded)
 };
 
 struct BwdParams {
@@ -55,6 +56,7 @@ struct SplitParams {
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_window_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_splitkv_bf16(const SplitParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_prep_bf16(const BwdParams& p, hipStream_t stream);

@@ -57,6 +57,13 @@ WORKLOADS = {
     "c5": Workload("c5", 2, 16, 16, 4096, 128, "bf16", True, False, True, 1.0, 5),
 }
 
+# Local-window workloads: the timed causal shape (c3) with a window instead of the causal mask.
+# window = (left, right): row i sees keys i - left .. i + right.
+WINDOW_WORKLOADS = {
+    "window": (Workload("window", 2, 16, 16, 8192, 128, "bf16", False, False, False, 0.5, 7),
+               (512, 512)),
+}
+
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum {
     FA_OK = 0,
@@ -79,6 +79,21 @@ typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  const int32_t* key_lens, int B, int Hq, int Hkv, int N, int d, float scale,
                  int causal, fa_dtype dtype, void* stream);
+
+/*
+ * Forward with a local attention window (tutorial page "Flash attention and efficient
+ * attention", section "Other Efficient Attention Variants", worked example "Local Attention
+ * Window"): query row i sees key j only when i - window_left <= j <= i + window_right (and
+ * j < key_lens[b]); a negative side means unbounded on that side (-1, -1 is plain attention,
+ * -1, 0 is causal; the page's window w is window_left = window_right = (w - 1) / 2).  The kernel
+ * visits only the key tiles each query tile's windows overlap, so the work is O(N w).
+ * Arguments otherwise as fa_fwd; only FA_BF16 with d in {64, 128}; a side below -1 is
+ * FA_ERR_SHAPE.
+ */
+fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* key_lens, int B, int Hq, int Hkv, int N, int d,
+                        float scale, int window_left, int window_right, fa_dtype dtype,
+                        void* stream);
 
 /*
  * Bytes of device workspace fa_bwd needs: two fp32 per query row (D_i = sum_c dO_ic O_ic and
