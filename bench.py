@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu-baseline]
     python bench.py --workload decode     (split-KV decode forward, GB/s against the HBM roofline)
+    python bench.py --workload window     (local-window forward, TFLOP/s on the visible pairs)
 
 One step = one pass of the whole hot path over one batch of synthetic inputs already resident
 in HBM: fa_fwd (O and LSE) then fa_bwd (its stages fa_bwd_prep, fa_bwd_dkdv, fa_bwd_dq), bf16 with
@@ -38,11 +39,13 @@ KERNEL_SRC = {                 # kernel -> sources whose hash guards stored coun
     "bwd_dkdv": [_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_device.h"],
     "bwd_dq": [_CSRC + "fa_bwd_dq.hip", _CSRC + "fa_device.h"],
     "splitkv": [_CSRC + "fa_splitkv.hip", _CSRC + "fa_device.h"],
+    "fwd_window": [_CSRC + "fa_fwd_bf16.hip", _CSRC + "fa_device.h"],
     "splitkv_merge": [_CSRC + "fa_splitkv.hip", _CSRC + "fa_device.h"],
 }
 # rocprofv3 kernel-name fragment -> kernel key
 KERNEL_MATCH = [("bwd_prep", "bwd_prep"), ("bwd_dkdv", "bwd_dkdv"), ("bwd_dq", "bwd_dq"),
-                ("fwd_bf16", "fwd_bf16"), ("splitkv_merge", "splitkv_merge"),
+                ("fwd_window", "fwd_window"), ("fwd_bf16", "fwd_bf16"),
+                ("splitkv_merge", "splitkv_merge"),
                 ("splitkv_bf16", "splitkv")]
 COPY_CALIB_BYTES = 1 << 30
 
@@ -98,6 +101,19 @@ def decode_kernel_bytes_compulsory(w, key_lens, splits, elem=2):
     part = splits * rows * (w.d + 1) * 4
     return {"splitkv": kv + rows * w.d * elem + part,
             "splitkv_merge": part + rows * w.d * elem + rows * 4}
+
+
+def window_pairs(N, left, right, key_lens=None, B=1):
+    """Number of visible (query, key) pairs of a local window, summed over the batches."""
+    import numpy as np
+    i = np.arange(N)
+    lo = np.maximum(i - left, 0) if left >= 0 else np.zeros(N, dtype=np.int64)
+    tot = 0
+    for b in range(B):
+        L = N if key_lens is None else int(key_lens[b])
+        hi = np.minimum(i + right, L - 1) if right >= 0 else np.full(N, L - 1)
+        tot += int(np.maximum(hi - lo + 1, 0).sum())
+    return tot
 
 
 def naive_bytes(B, Hq, N, elem=2):
@@ -179,6 +195,13 @@ def traffic_summary(d, workload, cmd_note):
         comp_note = ("Compulsory bytes: the range kernel reads the valid K and V rows once and Q "
                      "and writes each range's fp32 partial output and LSE; the merge reads those "
                      "and writes O and LSE.")
+    elif workload in fi.WINDOW_WORKLOADS:
+        w, window = fi.WINDOW_WORKLOADS[workload]
+        comp = {"fwd_window": fwd_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d)}
+        kernels = ("fwd_window",)
+        title = f"B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} local window {window} {w.dtype}"
+        comp_note = ("`vs compulsory` divides by the tiled IO count (read Q, K, V once, write O "
+                     "and LSE once).")
     else:
         w = fi.WORKLOADS[workload]
         comp = {"fwd_bf16": fwd_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d),
@@ -358,6 +381,76 @@ def bench_decode(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_window(args):
+    """Local-window forward on a windowed workload: one step = one fa_fwd_window call.  Work is
+    counted on the visible pairs only (4 d flops per pair per head: Q K^T and P V), so TFLOP/s
+    compare directly with the full forward's; the % of peak is against the bf16 MFMA peak."""
+    import torch
+
+    import exact_io_aware_68_amd as fa
+    import fa_inputs as fi
+    w, window = fi.WINDOW_WORKLOADS[args.workload]
+    x = fi.make(w)
+    dev = "cuda:0"
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        fa.fa_fwd_window(q, k, v, window=window, scale=x["scale"], o=o, lse=lse)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    pairs = window_pairs(w.N, window[0], window[1]) * w.B
+    flops = 4.0 * w.d * pairs * w.Hq
+    tf = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "local-window attention forward TFLOP/s on visible pairs + % bf16 MFMA peak",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"local window (left, right)={window}, B={w.B} H={w.Hq} N={w.N} "
+                               f"d={w.d}", "seed": w.seed, "parallelism": "single GPU"},
+        "visible_pairs_per_head": pairs // w.B, "flops": flops,
+        "full_attention_flops": fwd_flops(w.B, w.Hq, w.N, w.d, False),
+        "kernels_ms": {"fwd_window": round(ms, 4)},
+        "roofline": {"kernel": "fwd_window", "bound": "mfma", "achieved": round(tf, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": stored_traffic("fwd_window", args.workload)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import attn_fwd
+        t1 = time.perf_counter()
+        attn_fwd(x["q"][:1, :1], x["k"][:1, :1], x["v"][:1, :1], x["scale"], False, window=window)
+        dt = time.perf_counter() - t1
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        out["cpu_baseline"] = {"value": round(4.0 * w.d * (pairs // w.B) / dt / 1e12, 5),
+                               "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                               "sample": f"fp64 numpy oracle on 1 of {w.B * w.Hq} heads in "
+                                         f"{dt:.2f} s (visible-pair flops; the oracle forms full "
+                                         f"score rows); host affinity "
+                                         f"{len(os.sched_getaffinity(0))} cpus"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -390,6 +483,9 @@ def main():
     import fa_inputs as fi
     if args.workload in fi.DECODE_WORKLOADS:
         bench_decode(args)
+        return
+    if args.workload in fi.WINDOW_WORKLOADS:
+        bench_window(args)
         return
 
     import torch

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq",
             "fa_bwd_workspace_size", "fa_status_str", "fa_abi_version", "fa_fwd_splitkv",
-            "fa_fwd_splitkv_splits", "fa_fwd_splitkv_workspace_size"} <= set(names)
+            "fa_fwd_splitkv_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_window"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -159,6 +159,22 @@ def test_splitkv_plan_and_workspace(lib):
     assert fa.fa_fwd_splitkv_splits(4, 30, 8, 1, 16384) == 0           # Hq % Hkv != 0
 
 
+def win(lib, q=A, k=A, v=A, o=A, lse=A, kl=None, B=1, Hq=2, Hkv=1, N=64, d=128, scale=0.1,
+        left=16, right=16, dtype=fa.FA_BF16):
+    return lib.fa_fwd_window(q, k, v, o, lse, kl, B, Hq, Hkv, N, d, ctypes.c_float(scale), left,
+                             right, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(left=-2), SHAPE), (dict(right=-7), SHAPE), (dict(dtype=fa.FA_F32), DTYPE),
+    (dict(dtype=9), DTYPE), (dict(d=96), HEADDIM), (dict(Hq=3, Hkv=2), GQA),
+    (dict(scale=-1.0), SCALE), (dict(q=None), NULL), (dict(v=None), NULL), (dict(o=A + 8), ALIGN),
+    (dict(kl=A + 2), ALIGN), (dict(B=0, q=None), OK), (dict(N=0), OK),
+])
+def test_window_argument_errors_before_any_hip_call(lib, kw, code):
+    assert win(lib, **kw) == code
+
+
 def _gpu_present():
     import torch
     return torch.cuda.is_available()
@@ -169,4 +185,5 @@ def test_valid_call_without_device_reports_device_error(lib):
     assert fwd(lib) == DEVICE
     assert bwd(lib) == DEVICE
     assert skv(lib) == DEVICE
+    assert win(lib) == DEVICE
     assert fwd(lib, B=0) == OK              # empty problems never touch HIP at all
