@@ -63,13 +63,20 @@ def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
     return (h * Hkv) // Hq
 
 
-def visible_mask(rows: np.ndarray, L: int, causal: bool, window=None) -> np.ndarray:
+def visible_mask(rows: np.ndarray, L: int, causal: bool, window=None,
+                 block_mask=None) -> np.ndarray:
     """Boolean [len(rows), L]: key j is visible to query row i iff j < L and (not causal or j <= i)
     and, with window = (left, right), i - left <= j <= i + right (a negative side is unbounded).
 
     The window is the tutorial page's local attention window ("Other Efficient Attention
     Variants", worked example: w = 3 lets each token see itself and one neighbour on each side,
-    i.e. left = right = (w - 1) / 2)."""
+    i.e. left = right = (w - 1) / 2).
+
+    With block_mask = (bm, bq, bk), key j is visible to row i only if bm[i // bq][j // bk] is
+    nonzero: a tile-level bitmap over (query block, key block) pairs.  The study-note page
+    ("FlashAttention paper", What it does not claim) names block-sparse attention as a separate
+    extension and defines nothing more; the reading here is the plainest one, an element mask
+    that is constant on blocks, combined with the other masks."""
     j = np.arange(L)[None, :]
     i = np.asarray(rows)[:, None]
     vis = np.ones((len(rows), L), dtype=bool)
@@ -81,6 +88,10 @@ def visible_mask(rows: np.ndarray, L: int, causal: bool, window=None) -> np.ndar
             vis &= j >= i - left
         if right >= 0:
             vis &= j <= i + right
+    if block_mask is not None:
+        bm, bq, bk = block_mask
+        bm = np.asarray(bm) != 0
+        vis &= bm[np.asarray(rows)[:, None] // bq, j // bk]
     return vis
 
 
@@ -116,7 +127,7 @@ def _softmax_rows(s: np.ndarray, vis: np.ndarray):
 
 
 def attn_fwd(q, k, v, scale: float, causal: bool = False, key_lens=None,
-             heads=None, chunk: int = 1024, window=None):
+             heads=None, chunk: int = 1024, window=None, block_mask=None):
     """Exact attention forward.
 
     q: [B, Hq, N, d]; k, v: [B, Hkv, N, d] (any float type, widened to fp64).
@@ -124,6 +135,7 @@ def attn_fwd(q, k, v, scale: float, causal: bool = False, key_lens=None,
     ``heads``: optional iterable of (b, h) pairs to compute; other entries stay O = 0, LSE = nan.
     ``chunk``: query rows per block; chunking over query rows does not change any row's math.
     ``window``: optional (left, right) local window, see ``visible_mask``.
+    ``block_mask``: optional (bm, bq, bk) tile-level bitmap, see ``visible_mask``.
     """
     q, k, v = to64(q), to64(k), to64(v)
     B, Hq, N, d = q.shape
@@ -141,7 +153,7 @@ def attn_fwd(q, k, v, scale: float, causal: bool = False, key_lens=None,
         for r0 in range(0, N, chunk):
             rows = np.arange(r0, min(N, r0 + chunk))
             s = score_rows(q[b, h, rows], K, scale)
-            P, m, l = _softmax_rows(s, visible_mask(rows, L, causal, window))
+            P, m, l = _softmax_rows(s, visible_mask(rows, L, causal, window, block_mask))
             O[b, h, rows] = P @ V
             with np.errstate(divide="ignore"):
                 LSE[b, h, rows] = np.where(np.isfinite(m), m + np.log(np.where(l > 0, l, 1.0)),
@@ -180,7 +192,8 @@ def attn_decode(q, k, v, scale: float, key_lens=None):
     return O, LSE
 
 
-def attn_fwd_rows(q, k, v, scale: float, causal: bool, key_lens, picks, window=None):
+def attn_fwd_rows(q, k, v, scale: float, causal: bool, key_lens, picks, window=None,
+                  block_mask=None):
     """Forward for individual rows: ``picks`` is a list of (b, h, i).
 
     Returns (O_rows [len(picks), d], LSE_rows [len(picks)]).  Each row is computed on its own from
@@ -200,7 +213,7 @@ def attn_fwd_rows(q, k, v, scale: float, causal: bool, key_lens, picks, window=N
             cache[(b, g)] = (to64(k[b, g, :L]), to64(v[b, g, :L]))
         K, V = cache[(b, g)]
         s = score_rows(to64(q[b, h, i:i + 1]), K, scale)
-        P, m, l = _softmax_rows(s, visible_mask(np.array([i]), L, causal, window))
+        P, m, l = _softmax_rows(s, visible_mask(np.array([i]), L, causal, window, block_mask))
         O[n] = (P @ V)[0]
         LSE[n] = m[0] + np.log(l[0]) if np.isfinite(m[0]) else -np.inf
     return O, LSE
