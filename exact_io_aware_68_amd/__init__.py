@@ -15,6 +15,7 @@ The functions carry the C names (see include/fa.h for the full contract):
     fa_status_str, fa_abi_version
     fa_fwd_splitkv(q, k, v, *, scale, key_lens, num_splits, o, lse)  -> (o, lse)   (decode shapes)
     fa_fwd_window(q, k, v, *, window, scale, key_lens, o, lse)       -> (o, lse)   (local window)
+    fa_fwd_blocksparse(q, k, v, block_mask, *, scale, causal, key_lens, o, lse) -> (o, lse)
     fa_fwd_splitkv_splits, fa_fwd_splitkv_workspace_size
 
 Tensors are [B, H, N, d] contiguous ("BHND"); q/k/v/o/dO are bf16 (d in {64, 128}) or fp32
@@ -32,7 +33,10 @@ __all__ = [
     "fa_bwd_workspace_size", "fa_fwd_kernel_name", "fa_bwd_dkdv_kernel_name",
     "fa_bwd_dq_kernel_name", "fa_status_str", "fa_abi_version", "FA_F32", "FA_BF16",
     "fa_fwd_splitkv", "fa_fwd_splitkv_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_window",
+    "fa_fwd_blocksparse", "BLOCK_Q", "BLOCK_K",
 ]
+
+BLOCK_Q, BLOCK_K = 128, 64   # block-sparse bitmap granularity (query rows, keys)
 
 FA_F32, FA_BF16 = 0, 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +75,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_dq.restype = I
     lib.fa_bwd_workspace_size.argtypes = [I, I, I, I]
     lib.fa_bwd_workspace_size.restype = Z
+    lib.fa_fwd_blocksparse.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.fa_fwd_blocksparse.restype = I
     lib.fa_fwd_window.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, I, I, P]
     lib.fa_fwd_window.restype = I
     lib.fa_fwd_splitkv.argtypes = [P, P, P, P, P, P, P, Z, I, I, I, I, I, I, F, I, I, P]
@@ -201,6 +207,32 @@ def fa_fwd_window(q, k, v, *, window, scale: float | None = None, key_lens=None,
                               ctypes.c_float(_default_scale(d) if scale is None else scale),
                               int(left), int(right), _dtype_code(q), _stream(stream, q.device))
     _check("fa_fwd_window", st)
+    return o, lse
+
+
+def fa_fwd_blocksparse(q, k, v, block_mask, *, scale: float | None = None, causal: bool = False,
+                       key_lens=None, o=None, lse=None, want_lse: bool = True, stream=None):
+    """Block-sparse forward: block_mask is a uint8 device tensor [ceil(N/128), ceil(N/64)];
+    row i sees key j only where block_mask[i // 128, j // 64] != 0.  Returns (o, lse)."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shape(q, k)
+    for t in (q, k, v, block_mask):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    if block_mask.dtype != torch.uint8 or tuple(block_mask.shape) != (
+            -(-N // BLOCK_Q), -(-N // BLOCK_K)):
+        raise ValueError("block_mask must be uint8 [ceil(N/128), ceil(N/64)]")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if key_lens is not None and key_lens.dtype != torch.int32:
+        raise ValueError("key_lens must be int32")
+    st = load().fa_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(key_lens),
+                                   _ptr(block_mask), B, Hq, Hkv, N, d,
+                                   ctypes.c_float(_default_scale(d) if scale is None else scale),
+                                   int(causal), _dtype_code(q), _stream(stream, q.device))
+    _check("fa_fwd_blocksparse", st)
     return o, lse
 
 

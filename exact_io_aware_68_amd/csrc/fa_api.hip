@@ -130,6 +130,28 @@ fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, fl
     return launched(fa::launch_fwd_window_bf16(p, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int32_t* key_lens, const uint8_t* block_mask, int B, int Hq,
+                             int Hkv, int N, int d, float scale, int causal, fa_dtype dtype,
+                             void* stream) {
+    if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_DTYPE;
+    fa_status st = check_shape(B, Hq, Hkv, N, d);
+    if (st != FA_OK) return st;
+    if (N > 65536) return FA_ERR_SHAPE;
+    if (dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if ((st = check_scale(scale)) != FA_OK) return st;
+    if (B == 0 || N == 0) return FA_OK;
+    if (!q || !k || !v || !o || !block_mask) return FA_ERR_NULL;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+        misaligned(lse, 4) || misaligned(key_lens, 4))
+        return FA_ERR_ALIGN;
+    if ((st = device_ready()) != FA_OK) return st;
+    fa::FwdParams p{q, k, v, o, lse, key_lens, B, Hq, Hkv, N, d, scale, causal ? 1 : 0, -1, -1,
+                    block_mask};
+    return launched(fa::launch_fwd_sparse_bf16(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t fa_bwd_workspace_size(int B, int Hq, int N, int d) {
     if (B < 0 || Hq <= 0 || N < 0 || d <= 0) return 0;
     return (size_t)B * (size_t)Hq * (size_t)N * 2 * sizeof(float);

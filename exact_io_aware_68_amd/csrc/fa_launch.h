@@ -18,6 +18,7 @@ struct FwdParams {
     float scale;
     int causal;
     int wl = -1, wr = -1;     // local window: row i sees keys i - wl .. i + wr (-1: unbounded)
+    const uint8_t* block_mask = nullptr;   // block-sparse: [ceil(N/128)][ceil(N/64)] bitmap
 };
 
 struct BwdParams {
@@ -57,6 +58,7 @@ struct SplitParams {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_window_bf16(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_sparse_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_splitkv_bf16(const SplitParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_prep_bf16(const BwdParams& p, hipStream_t stream);

@@ -64,6 +64,28 @@ WINDOW_WORKLOADS = {
                (512, 512)),
 }
 
+# Block-sparse workloads: a shape and the recipe of its bitmap (see ``block_bitmap``).
+SPARSE_WORKLOADS = {
+    "sparse": (Workload("sparse", 2, 16, 16, 8192, 128, "bf16", False, False, False, 0.5, 8),
+               0.2),
+}
+
+
+def block_bitmap(N: int, density: float, seed: int, band: int = 2, bq: int = 128,
+                 bk: int = 64) -> torch.Tensor:
+    """uint8 [ceil(N/bq), ceil(N/bk)] bitmap: the key blocks within ``band`` blocks of each query
+    block's diagonal, plus every other block independently with probability ``density`` (CPU
+    generator seeded with ``seed``)."""
+    nq, nk = -(-N // bq), -(-N // bk)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    bm = (torch.rand(nq, nk, generator=g) < density)
+    qb = torch.arange(nq)[:, None] * (bq // bk)
+    kb = torch.arange(nk)[None, :]
+    bm |= (kb >= qb - band) & (kb <= qb + (bq // bk) - 1 + band)
+    return bm.to(torch.uint8)
+
+
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 

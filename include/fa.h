@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum {
     FA_OK = 0,
@@ -94,6 +94,20 @@ fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, fl
                         const int32_t* key_lens, int B, int Hq, int Hkv, int N, int d,
                         float scale, int window_left, int window_right, fa_dtype dtype,
                         void* stream);
+
+/*
+ * Block-sparse forward (the extension the study-note page "FlashAttention paper", section "What
+ * it does not claim", names without defining): block_mask is a device bitmap of uint8, one byte
+ * per (query block of 128 rows, key block of 64 keys), row-major [ceil(N/128)][ceil(N/64)],
+ * shared by every batch and head; query row i sees key j only when
+ * block_mask[i / 128][j / 64] != 0, on top of the causal mask and key_lens.  Blocks that are
+ * off are never loaded or multiplied.  A row with no visible key gets O = 0, LSE = -inf.
+ * Arguments otherwise as fa_fwd; only FA_BF16 with d in {64, 128}; N <= 65536.
+ */
+fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int32_t* key_lens, const uint8_t* block_mask, int B, int Hq,
+                             int Hkv, int N, int d, float scale, int causal, fa_dtype dtype,
+                             void* stream);
 
 /*
  * Bytes of device workspace fa_bwd needs: two fp32 per query row (D_i = sum_c dO_ic O_ic and

@@ -30,7 +30,8 @@ def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq",
             "fa_bwd_workspace_size", "fa_status_str", "fa_abi_version", "fa_fwd_splitkv",
-            "fa_fwd_splitkv_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_window"} <= set(names)
+            "fa_fwd_splitkv_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_window",
+            "fa_fwd_blocksparse"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -175,6 +176,22 @@ def test_window_argument_errors_before_any_hip_call(lib, kw, code):
     assert win(lib, **kw) == code
 
 
+def bsp(lib, q=A, k=A, v=A, o=A, lse=A, kl=None, bm=A, B=1, Hq=2, Hkv=1, N=256, d=128,
+        scale=0.1, causal=0, dtype=fa.FA_BF16):
+    return lib.fa_fwd_blocksparse(q, k, v, o, lse, kl, bm, B, Hq, Hkv, N, d, ctypes.c_float(scale),
+                                  causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bm=None), NULL), (dict(q=None), NULL), (dict(N=65537), SHAPE), (dict(N=-1), SHAPE),
+    (dict(dtype=fa.FA_F32), DTYPE), (dict(d=32), HEADDIM), (dict(Hq=5, Hkv=2), GQA),
+    (dict(scale=0.0), SCALE), (dict(k=A + 4), ALIGN), (dict(lse=A + 2), ALIGN),
+    (dict(B=0, bm=None), OK), (dict(N=0), OK),
+])
+def test_blocksparse_argument_errors_before_any_hip_call(lib, kw, code):
+    assert bsp(lib, **kw) == code
+
+
 def _gpu_present():
     import torch
     return torch.cuda.is_available()
@@ -186,4 +203,5 @@ def test_valid_call_without_device_reports_device_error(lib):
     assert bwd(lib) == DEVICE
     assert skv(lib) == DEVICE
     assert win(lib) == DEVICE
+    assert bsp(lib) == DEVICE
     assert fwd(lib, B=0) == OK              # empty problems never touch HIP at all

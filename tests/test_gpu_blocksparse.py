@@ -1,0 +1,112 @@
+"""GPU parity of fa_fwd_blocksparse (through the C ABI) against the oracle's block-sparse forward."""
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_68_amd as fa
+import fa_inputs as fi
+from oracle import attn_fwd, attn_fwd_rows
+from tests._parity import TOL_BF16_MAX, TOL_BF16_MEAN, TOL_LSE, check_close, np64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def gen(B, Hq, Hkv, N, d, seed, padded=False):
+    return fi.make(fi.Workload("t", B, Hq, Hkv, N, d, "bf16", False, padded, False, 1.0, seed))
+
+
+def run(x, bm, causal):
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    kl = None if x.get("key_lens") is None else x["key_lens"].to(DEV)
+    o, lse = fa.fa_fwd_blocksparse(q, k, v, bm.to(DEV), scale=x["scale"], causal=causal,
+                                   key_lens=kl)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check(x, bm, causal, o, lse):
+    O, LSE = attn_fwd(x["q"], x["k"], x["v"], x["scale"], causal, x["key_lens"],
+                      block_mask=(bm.numpy(), fa.BLOCK_Q, fa.BLOCK_K))
+    rows = np.isfinite(LSE)
+    check_close("O", np64(o), O, TOL_BF16_MAX, TOL_BF16_MEAN)
+    check_close("LSE", np64(lse)[rows], LSE[rows], TOL_LSE)
+    assert np.all(np.isneginf(np64(lse)[~rows])) and np.all(np64(o)[~rows] == 0)
+
+
+CASES = [  # (B, Hq, Hkv, N, d, density, causal, padded)
+    (2, 2, 2, 512, 128, 0.3, False, False),
+    (2, 4, 2, 700, 128, 0.5, True, True),
+    (1, 2, 1, 1000, 64, 0.2, False, True),
+    (2, 2, 2, 300, 64, 0.7, True, False),
+    (1, 2, 2, 129, 128, 0.4, False, False),
+    (1, 4, 4, 1500, 128, 0.1, True, False),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,density,causal,padded", CASES)
+def test_blocksparse_parity(B, Hq, Hkv, N, d, density, causal, padded):
+    print(f"\nblocksparse B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} density={density} causal={causal}",
+          flush=True)
+    x = gen(B, Hq, Hkv, N, d, 800 + N + d, padded)
+    g = torch.Generator().manual_seed(N)
+    bm = (torch.rand(-(-N // 128), -(-N // 64), generator=g) < density).to(torch.uint8)
+    o, lse = run(x, bm, causal)
+    check(x, bm, causal, o, lse)
+
+
+def test_all_on_equals_the_dense_forward():
+    x = gen(2, 2, 1, 600, 128, 41, padded=True)
+    bm = torch.ones(5, 10, dtype=torch.uint8)
+    for causal in (False, True):
+        o, lse = run(x, bm, causal)
+        check(x, bm, causal, o, lse)
+        q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+        o2, l2 = fa.fa_fwd(q, k, v, scale=x["scale"], causal=causal, key_lens=x["key_lens"].to(DEV))
+        torch.cuda.synchronize()
+        assert (o.float() - o2.float()).abs().max().item() <= 2 * TOL_BF16_MAX
+        assert (lse - l2).abs().max().item() <= 2 * TOL_LSE
+
+
+def test_rows_with_every_block_off_and_empty_bitmap():
+    x = gen(1, 2, 2, 384, 64, 42)
+    bm = torch.zeros(3, 6, dtype=torch.uint8)
+    bm[1, 3] = 1                   # rows 128..255 see keys 192..255 only
+    o, lse = run(x, bm, False)
+    check(x, bm, False, o, lse)
+    assert torch.all(o[:, :, :128] == 0) and torch.all(torch.isneginf(lse[:, :, 256:]))
+    o, lse = run(x, torch.zeros(3, 6, dtype=torch.uint8), False)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_nan_in_skipped_blocks_and_padding_never_reaches_outputs():
+    x = gen(1, 2, 2, 512, 128, 43)
+    x["key_lens"] = torch.tensor([450], dtype=torch.int32)
+    bm = torch.ones(4, 8, dtype=torch.uint8)
+    bm[:, 2] = 0
+    o_ref, l_ref = run(x, bm, False)
+    x["k"][:, :, 128:192] = float("nan")     # key block 2: off for every row
+    x["v"][:, :, 128:192] = float("nan")
+    x["k"][:, :, 450:] = float("nan")
+    x["v"][:, :, 450:] = float("nan")
+    o, lse = run(x, bm, False)
+    assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+
+
+def test_sparse_workload_sampled_rows():
+    w, density = fi.SPARSE_WORKLOADS["sparse"]
+    print(f"\nsparse workload B={w.B} H={w.Hq} N={w.N} d={w.d} density={density}", flush=True)
+    x = fi.make(w)
+    bm = fi.block_bitmap(w.N, density, w.seed)
+    o, lse = run(x, bm, w.causal)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    r = np.random.default_rng(w.seed)
+    picks = sorted({(b, h, i) for b in range(w.B) for h in (0, w.Hq - 1)
+                    for i in (0, 127, 128, 4095, w.N - 1)} |
+                   {(int(r.integers(w.B)), int(r.integers(w.Hq)), int(r.integers(w.N)))
+                    for _ in range(48)})
+    O, LSE = attn_fwd_rows(x["q"], x["k"], x["v"], x["scale"], w.causal, None, picks,
+                           block_mask=(bm.numpy(), fa.BLOCK_Q, fa.BLOCK_K))
+    idx = tuple(torch.tensor(a) for a in zip(*picks))
+    check_close("O", np64(o[idx]), O, TOL_BF16_MAX, TOL_BF16_MEAN)
+    check_close("LSE", np64(lse[idx]), LSE, TOL_LSE)
