@@ -4,6 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu-baseline]
     python bench.py --workload decode     (split-KV decode forward, GB/s against the HBM roofline)
     python bench.py --workload window     (local-window forward, TFLOP/s on the visible pairs)
+    python bench.py --workload sparse     (block-sparse forward, TFLOP/s on the visible pairs)
 
 One step = one pass of the whole hot path over one batch of synthetic inputs already resident
 in HBM: fa_fwd (O and LSE) then fa_bwd (its stages fa_bwd_prep, fa_bwd_dkdv, fa_bwd_dq), bf16 with
@@ -40,11 +41,12 @@ KERNEL_SRC = {                 # kernel -> sources whose hash guards stored coun
     "bwd_dq": [_CSRC + "fa_bwd_dq.hip", _CSRC + "fa_device.h"],
     "splitkv": [_CSRC + "fa_splitkv.hip", _CSRC + "fa_device.h"],
     "fwd_window": [_CSRC + "fa_fwd_bf16.hip", _CSRC + "fa_device.h"],
+    "fwd_sparse": [_CSRC + "fa_fwd_sparse.hip", _CSRC + "fa_device.h"],
     "splitkv_merge": [_CSRC + "fa_splitkv.hip", _CSRC + "fa_device.h"],
 }
 # rocprofv3 kernel-name fragment -> kernel key
 KERNEL_MATCH = [("bwd_prep", "bwd_prep"), ("bwd_dkdv", "bwd_dkdv"), ("bwd_dq", "bwd_dq"),
-                ("fwd_window", "fwd_window"), ("fwd_bf16", "fwd_bf16"),
+                ("fwd_window", "fwd_window"), ("fwd_sparse", "fwd_sparse"), ("fwd_bf16", "fwd_bf16"),
                 ("splitkv_merge", "splitkv_merge"),
                 ("splitkv_bf16", "splitkv")]
 COPY_CALIB_BYTES = 1 << 30
@@ -113,6 +115,23 @@ def window_pairs(N, left, right, key_lens=None, B=1):
         L = N if key_lens is None else int(key_lens[b])
         hi = np.minimum(i + right, L - 1) if right >= 0 else np.full(N, L - 1)
         tot += int(np.maximum(hi - lo + 1, 0).sum())
+    return tot
+
+
+def sparse_pairs(N, bm, causal, bq=128, bk=64):
+    """Visible (query, key) pairs of one head under a block bitmap (and causal), exactly."""
+    import numpy as np
+    bm = np.asarray(bm) != 0
+    tot = 0
+    for qb in range(bm.shape[0]):
+        r0, r1 = qb * bq, min(N, (qb + 1) * bq)
+        for kb in np.nonzero(bm[qb])[0]:
+            k0, k1 = int(kb) * bk, min(N, (int(kb) + 1) * bk)
+            if not causal:
+                tot += int((r1 - r0) * (k1 - k0))
+            else:
+                rows = np.arange(r0, r1)
+                tot += int(np.clip(rows - k0 + 1, 0, k1 - k0).sum())
     return tot
 
 
@@ -195,6 +214,14 @@ def traffic_summary(d, workload, cmd_note):
         comp_note = ("Compulsory bytes: the range kernel reads the valid K and V rows once and Q "
                      "and writes each range's fp32 partial output and LSE; the merge reads those "
                      "and writes O and LSE.")
+    elif workload in fi.SPARSE_WORKLOADS:
+        w, density = fi.SPARSE_WORKLOADS[workload]
+        comp = {"fwd_sparse": fwd_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d)}
+        kernels = ("fwd_sparse",)
+        title = (f"B={w.B} Hq={w.Hq} N={w.N} d={w.d} block bitmap band 2 + random {density} "
+                 f"{w.dtype}")
+        comp_note = ("`vs compulsory` divides by the tiled IO count (read Q, K, V once, write O "
+                     "and LSE once).")
     elif workload in fi.WINDOW_WORKLOADS:
         w, window = fi.WINDOW_WORKLOADS[workload]
         comp = {"fwd_window": fwd_bytes_compulsory(w.B, w.Hq, w.Hkv, w.N, w.d)}
@@ -451,6 +478,80 @@ def bench_window(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_sparse(args):
+    """Block-sparse forward on a sparse workload: one step = one fa_fwd_blocksparse call.  Work is
+    counted on the visible pairs of the bitmap (4 d flops per pair per head)."""
+    import torch
+
+    import exact_io_aware_68_amd as fa
+    import fa_inputs as fi
+    w, density = fi.SPARSE_WORKLOADS[args.workload]
+    x = fi.make(w)
+    bm_cpu = fi.block_bitmap(w.N, density, w.seed)
+    dev = "cuda:0"
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    bm = bm_cpu.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        fa.fa_fwd_blocksparse(q, k, v, bm, scale=x["scale"], causal=w.causal, o=o, lse=lse)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    pairs = sparse_pairs(w.N, bm_cpu.numpy(), w.causal)
+    flops = 4.0 * w.d * pairs * w.B * w.Hq
+    tf = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "block-sparse attention forward TFLOP/s on visible pairs + % bf16 MFMA peak",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"block-sparse bitmap (128x64 blocks, band 2 + random {density}) "
+                               f"B={w.B} H={w.Hq} N={w.N} d={w.d} causal={w.causal}",
+                   "seed": w.seed, "parallelism": "single GPU"},
+        "active_blocks": int(bm_cpu.sum()), "blocks": int(bm_cpu.numel()),
+        "visible_pairs_per_head": pairs, "flops": flops,
+        "full_attention_flops": fwd_flops(w.B, w.Hq, w.N, w.d, w.causal),
+        "kernels_ms": {"fwd_sparse": round(ms, 4)},
+        "roofline": {"kernel": "fwd_sparse", "bound": "mfma", "achieved": round(tf, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": stored_traffic("fwd_sparse", args.workload)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import attn_fwd
+        t1 = time.perf_counter()
+        attn_fwd(x["q"][:1, :1], x["k"][:1, :1], x["v"][:1, :1], x["scale"], w.causal,
+                 block_mask=(bm_cpu.numpy(), 128, 64))
+        dt = time.perf_counter() - t1
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        out["cpu_baseline"] = {"value": round(4.0 * w.d * pairs / dt / 1e12, 5),
+                               "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                               "sample": f"fp64 numpy oracle on 1 of {w.B * w.Hq} heads in "
+                                         f"{dt:.2f} s (visible-pair flops; the oracle forms full "
+                                         f"score rows); host affinity "
+                                         f"{len(os.sched_getaffinity(0))} cpus"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -486,6 +587,9 @@ def main():
         return
     if args.workload in fi.WINDOW_WORKLOADS:
         bench_window(args)
+        return
+    if args.workload in fi.SPARSE_WORKLOADS:
+        bench_sparse(args)
         return
 
     import torch
