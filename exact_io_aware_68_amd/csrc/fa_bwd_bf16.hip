@@ -183,95 +183,112 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
             // Waves whose keys all lie above the diagonal of this tile (only on a workgroup's
             // first query tile) run it anyway: the causal mask makes P = 0, so dS = 0 and the
             // accumulators are unchanged; a branch here would cost more in register copies.
+            //
+            // The tile's 64 query rows are two 32-row halves h, and the products run in four
+            // phases so that the VALU work of one half runs alongside MFMAs of the other:
+            //   A: S, dP of half 0;   B: S, dP of half 1      + P, dS of half 0 (VALU);
+            //   C: dV, dK of half 0   + P, dS of half 1 (VALU);   D: dV, dK of half 1.
+            // Within a phase the LDS operands of MFMA step k+1 are read while step k runs, and
+            // one scheduling fence per step keeps that order (without it the scheduler sinks
+            // each read next to its MFMA and serialises one LDS round trip per MFMA).
             {
-                // S = Q K^T and dP = dO V^T; C row r -> query 32 q2 + 8(r/4) + 4hh + r%4, column -> key.
-                f32x16 sa[2] = {f32x16{}, f32x16{}};
-                f32x16 pa[2] = {f32x16{}, f32x16{}};
-                // Operands of reduction step s+1 are read while the MFMAs of step s run; the
-                // fence per step keeps the scheduler from sinking each read next to its MFMA
-                // (which serialises one LDS round trip per MFMA).
-                bf16x8 cq[2], co[2];
-                auto rd = [&](int s, bf16x8 (&aq)[2], bf16x8 (&ao)[2]) {
-#pragma unroll
-                    for (int q2 = 0; q2 < 2; ++q2) {
-                        const int ro = 32 * q2 * D + qro[s];
-                        aq[q2] = __builtin_bit_cast(bf16x8, ld16(Qc + ro));
-                        ao[q2] = __builtin_bit_cast(bf16x8, ld16(Oc + ro));
-                    }
-                };
-                rd(0, cq, co);
-#pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    bf16x8 nq[2], no[2];
-                    if (s + 1 < NS) rd(s + 1, nq, no);
-#pragma unroll
-                    for (int q2 = 0; q2 < 2; ++q2) {
-                        sa[q2] = mfma32(cq[q2], kf[s], sa[q2]);
-                        pa[q2] = mfma32(co[q2], vf[s], pa[q2]);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (s + 1 < NS) {
-#pragma unroll
-                        for (int q2 = 0; q2 < 2; ++q2) {
-                            cq[q2] = nq[q2];
-                            co[q2] = no[q2];
-                        }
-                    }
-                }
-                // Phase fences keep the scheduler from hoisting the next phase's LDS reads
-                // across this one, which would push the live registers past the VGPR file.
-                __builtin_amdgcn_sched_barrier(0);
-                // P = 2^(S C - LSE2) and dS = P (dP - D) (the scale of dK is applied at the end).
                 const bool need_mask = (CAUSAL && kw0 + 31 > i0) || (kw0 + 32 > Lk);
-#pragma unroll
-                for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int ql = 32 * q2 + 8 * g + 4 * hh;
-                        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.l2[cur][ql]);
-                        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dd[cur][ql]);
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) {
-                            const int r = 4 * g + x;
-                            float pv = exp2_hw(__builtin_fmaf(sa[q2][r], Cs, -l4[x]));
-                            if (need_mask) {
-                                const bool hide = key >= Lk || (CAUSAL && key > i0 + ql + x);
-                                pv = hide ? 0.f : pv;
-                            }
-                            sa[q2][r] = pv;
-                            pa[q2][r] = pv * (pa[q2][r] - d4[x]);
-                        }
-                    }
-                bf16x8 pf[4], sf[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int q2 = u >> 1, o8 = 8 * (u & 1);
-                    pf[u] = to_bf16x8(sa[q2][o8], sa[q2][o8 + 1], sa[q2][o8 + 2], sa[q2][o8 + 3],
-                                      sa[q2][o8 + 4], sa[q2][o8 + 5], sa[q2][o8 + 6], sa[q2][o8 + 7]);
-                    sf[u] = to_bf16x8(pa[q2][o8], pa[q2][o8 + 1], pa[q2][o8 + 2], pa[q2][o8 + 3],
-                                      pa[q2][o8 + 4], pa[q2][o8 + 5], pa[q2][o8 + 6], pa[q2][o8 + 7]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                // dV^T += dO^T P, dK^T += Q^T dS: A = one d-column over 8 query rows.
-                // Same read-ahead as above, one (dt, u) pair of products at a time.
-                bf16x8 ao, aq;
-                auto rdt = [&](int g, bf16x8& o_, bf16x8& q_) {
-                    const int dt = g / 4, ru = 16 * (g % 4) * D;
+                // S = Q K^T, dP = dO V^T per half; C row r -> query 32h + 8(r/4) + 4hh + r%4,
+                // column -> key.
+                f32x16 sa[2], pa[2];
+                bf16x8 pf[4], sf[4];   // B operands of dV, dK for query groups u = 2h + 0/1
+                auto rdh = [&](int h, int k, bf16x8& q_, bf16x8& o_) {   // A operands, step k
+                    const int ro = 32 * h * D + qro[k];
+                    q_ = __builtin_bit_cast(bf16x8, ld16(Qc + ro));
+                    o_ = __builtin_bit_cast(bf16x8, ld16(Oc + ro));
+                };
+                auto rdt = [&](int h, int g, bf16x8& o_, bf16x8& q_) {   // dO^T, Q^T, step g
+                    const int dt = g >> 1, ru = 16 * (2 * h + (g & 1)) * D;
                     o_ = trop(Oc + ru, tro[dt][0], tro[dt][1]);
                     q_ = trop(Qc + ru, tro[dt][0], tro[dt][1]);
                 };
-                rdt(0, ao, aq);
+                // Row statistics (LSE2, D) of half h, read from LDS once per half before its
+                // VALU phase (reads inside the phase put LDS latency on the VALU's path).
+                f32x4 l4[4], d4[4];
+                auto load_stats = [&](int h) {
 #pragma unroll
-                for (int g = 0; g < 4 * ND; ++g) {
-                    bf16x8 no, nq;
-                    if (g + 1 < 4 * ND) rdt(g + 1, no, nq);
-                    const int dt = g / 4, u = g % 4;
-                    dva[dt] = mfma32(ao, pf[u], dva[dt]);
-                    dka[dt] = mfma32(aq, sf[u], dka[dt]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (g + 1 < 4 * ND) {
-                        ao = no;
-                        aq = nq;
+                    for (int g = 0; g < 4; ++g) {
+                        const int ql = 32 * h + 8 * g + 4 * hh;
+                        l4[g] = *reinterpret_cast<const f32x4*>(&sm.l2[cur][ql]);
+                        d4[g] = *reinterpret_cast<const f32x4*>(&sm.dd[cur][ql]);
+                    }
+                };
+                // P = 2^(S C - LSE2) and dS = P (dP - D) for scores r0 .. r0 + n - 1 of half h
+                // (the scale of dK is applied at the end).
+                auto softmax_grad = [&](int h, int r0, int n) {
+                    for (int r = r0; r < r0 + n; ++r) {
+                        const int ql = 32 * h + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        float pv = exp2_hw(__builtin_fmaf(sa[h][r], Cs, -l4[r >> 2][r & 3]));
+                        if (need_mask) {
+                            const bool hide = key >= Lk || (CAUSAL && key > i0 + ql);
+                            pv = hide ? 0.f : pv;
+                        }
+                        sa[h][r] = pv;
+                        pa[h][r] = pv * (pa[h][r] - d4[r >> 2][r & 3]);
+                    }
+                };
+                auto to_operands = [&](int h, int uu) {
+                    const int u = 2 * h + uu, o8 = 8 * uu;
+                    pf[u] = to_bf16x8(sa[h][o8], sa[h][o8 + 1], sa[h][o8 + 2], sa[h][o8 + 3],
+                                      sa[h][o8 + 4], sa[h][o8 + 5], sa[h][o8 + 6], sa[h][o8 + 7]);
+                    sf[u] = to_bf16x8(pa[h][o8], pa[h][o8 + 1], pa[h][o8 + 2], pa[h][o8 + 3],
+                                      pa[h][o8 + 4], pa[h][o8 + 5], pa[h][o8 + 6], pa[h][o8 + 7]);
+                };
+                constexpr int EB = 16 / NS;         // scores per S/dP step of phase B
+                constexpr int EC = 16 / (2 * ND);   // scores per dV/dK step of phase C
+                // Phases A and B: S, dP of half h (MFMA), with half 0's softmax gradient in B.
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    if (h == 1) load_stats(0);
+                    sa[h] = f32x16{};
+                    pa[h] = f32x16{};
+                    bf16x8 cq, co;
+                    rdh(h, 0, cq, co);
+#pragma unroll
+                    for (int k = 0; k < NS; ++k) {
+                        bf16x8 nq, no;
+                        if (k + 1 < NS) rdh(h, k + 1, nq, no);
+                        sa[h] = mfma32(cq, kf[k], sa[h]);
+                        pa[h] = mfma32(co, vf[k], pa[h]);
+                        if (h == 1) {
+                            softmax_grad(0, EB * k, EB);
+                            if ((EB * (k + 1)) % 8 == 0) to_operands(0, EB * (k + 1) / 8 - 1);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (k + 1 < NS) {
+                            cq = nq;
+                            co = no;
+                        }
+                    }
+                }
+                // Phases C and D: dV^T += dO^T P, dK^T += Q^T dS of half h (A = one d-column
+                // over 8 query rows), with half 1's softmax gradient in C.
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    if (h == 0) load_stats(1);
+                    bf16x8 ao, aq;
+                    rdt(h, 0, ao, aq);
+#pragma unroll
+                    for (int g = 0; g < 2 * ND; ++g) {
+                        bf16x8 no, nq;
+                        if (g + 1 < 2 * ND) rdt(h, g + 1, no, nq);
+                        const int dt = g >> 1, u = 2 * h + (g & 1);
+                        dva[dt] = mfma32(ao, pf[u], dva[dt]);
+                        dka[dt] = mfma32(aq, sf[u], dka[dt]);
+                        if (h == 0) {
+                            softmax_grad(1, EC * g, EC);
+                            if ((EC * (g + 1)) % 8 == 0) to_operands(1, EC * (g + 1) / 8 - 1);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (g + 1 < 2 * ND) {
+                            ao = no;
+                            aq = nq;
+                        }
                     }
                 }
             }
