@@ -56,6 +56,13 @@ struct Flag {
     static constexpr bool value = B;
 };
 
+// Position of a step within a run of four (-1: known only at run time).  With the position
+// fixed at compile time the LDS buffers a step reads and fills are constant addresses.
+template <int P>
+struct Phase {
+    static constexpr int value = P;
+};
+
 template <int D>
 struct FwdLds {
     bf16 k[2][kLT * D];   // swizzled K tiles (shifted by 32 keys), double-buffered
@@ -275,20 +282,20 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
     const int nkt = kend > kBC ? (kend - kBC + kLT - 1) / kLT : 0;  // shifted K tiles
     const bf16* __restrict__ Kr = K + (size_t)kb * D;
     const bf16* __restrict__ Vr = V + (size_t)kb * D;
-    auto load_k = [&](int T) {   // shifted K tile T: keys kb + 64 T + 32 .. kb + 64 T + 95
+    auto load_k = [&](int T, int buf) {   // shifted K tile T: keys kb + 64 T + 32 .. + 95
         const int k0 = T * kLT + kBC;
-        dma_tile<D, kLT, kWaves>(Kr + (size_t)k0 * D, Lr - k0, sm.k[T & 1], w, lane);
+        dma_tile<D, kLT, kWaves>(Kr + (size_t)k0 * D, Lr - k0, sm.k[buf], w, lane);
     };
-    auto load_v = [&](int T) {
+    auto load_v = [&](int T, int buf) {
         const int k0 = T * kLT;
-        dma_tile<D, kLT, kWaves>(Vr + (size_t)k0 * D, Lr - k0, sm.v[T & 1], w, lane);
+        dma_tile<D, kLT, kWaves>(Vr + (size_t)k0 * D, Lr - k0, sm.v[buf], w, lane);
     };
     f32x16 sa[NH][kNT], sb[NH][kNT];
     bf16x8 pf[NH][kNT][2];
     if (ntiles > 0) {
         dma_tile<D, kBC, kWaves>(Kr, Lr, sm.k[1] + kBC * D, w, lane);   // keys kb .. kb + 31
-        load_v(0);
-        if (nkt > 0) load_k(0);
+        load_v(0, 0);
+        if (nkt > 0) load_k(0, 0);
     }
     wait_vmem();
     __syncthreads();
@@ -311,17 +318,21 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
     }
     __syncthreads();   // keys 0..31 in buffer 1 are overwritten by K tile 1 during steps 0, 1
 
-    auto step = [&](auto maskn, auto odd, int j, f32x16 (&cur)[NH][kNT],
+    auto step = [&](auto maskn, auto odd, auto ph, int j, f32x16 (&cur)[NH][kNT],
                     f32x16 (&nxt)[NH][kNT]) {
+        constexpr int P = decltype(ph)::value;
         const int T = j >> 1;
+        // LDS buffer of tile T and the half of it that step j reads
+        const int tb = P < 0 ? T & 1 : (P >> 1) & 1;
+        const int half = P < 0 ? j & 1 : P & 1;
         if constexpr (!decltype(odd)::value) {   // buffers (T+1)&1 were released at the last barrier
-            if (T + 1 < nkt) load_k(T + 1);
-            if (T + 1 < nlt) load_v(T + 1);
+            if (T + 1 < nkt) load_k(T + 1, tb ^ 1);
+            if (T + 1 < nlt) load_v(T + 1, tb ^ 1);
         }
-        scores(ksub(j + 1), nxt);                           // MFMA ...
+        scores(sm.k[tb] + half * kBC * D, nxt);             // MFMA (= ksub(j + 1)) ...
         exponentiate(cur, pf);                              // ... alongside VALU
         if constexpr (decltype(maskn)::value) mask(j + 1, nxt);
-        pv(vsub(j), pf);
+        pv(sm.v[tb] + half * kBC * D, pf);                  // (= vsub(j))
         if constexpr (decltype(odd)::value) {
             wait_vmem();       // this wave's share of tiles T+1 has landed
             __syncthreads();   // tiles T+1 visible; buffers T&1 free
@@ -333,24 +344,31 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
         // per-pair choice between masked and unmasked bodies measured slower: the two bodies
         // pushed the kernel past the register file).
         for (; j + 2 < ntiles; j += 2) {
-            step(Flag<true>{}, Flag<false>{}, j, sa, sb);
-            step(Flag<true>{}, Flag<true>{}, j + 1, sb, sa);
+            step(Flag<true>{}, Flag<false>{}, Phase<-1>{}, j, sa, sb);
+            step(Flag<true>{}, Flag<true>{}, Phase<-1>{}, j + 1, sb, sa);
         }
     } else {
         // Steps below jfree need no mask for any row of the workgroup.
         int jfree = Lk / kBC;
         if (CAUSAL) jfree = min(jfree, (qt * kBR + 1) / kBC);
+        // j is a multiple of 4 in this loop: fixed buffers, constant LDS addresses
+        for (; j + 4 < ntiles && j + 4 < jfree; j += 4) {
+            step(Flag<false>{}, Flag<false>{}, Phase<0>{}, j, sa, sb);
+            step(Flag<false>{}, Flag<true>{}, Phase<1>{}, j + 1, sb, sa);
+            step(Flag<false>{}, Flag<false>{}, Phase<2>{}, j + 2, sa, sb);
+            step(Flag<false>{}, Flag<true>{}, Phase<3>{}, j + 3, sb, sa);
+        }
         for (; j + 2 < ntiles && j + 2 < jfree; j += 2) {
-            step(Flag<false>{}, Flag<false>{}, j, sa, sb);
-            step(Flag<false>{}, Flag<true>{}, j + 1, sb, sa);
+            step(Flag<false>{}, Flag<false>{}, Phase<-1>{}, j, sa, sb);
+            step(Flag<false>{}, Flag<true>{}, Phase<-1>{}, j + 1, sb, sa);
         }
         for (; j + 2 < ntiles; j += 2) {
-            step(Flag<true>{}, Flag<false>{}, j, sa, sb);
-            step(Flag<true>{}, Flag<true>{}, j + 1, sb, sa);
+            step(Flag<true>{}, Flag<false>{}, Phase<-1>{}, j, sa, sb);
+            step(Flag<true>{}, Flag<true>{}, Phase<-1>{}, j + 1, sb, sa);
         }
     }
     if (j + 1 < ntiles) {
-        step(Flag<true>{}, Flag<false>{}, j, sa, sb);   // no loads left: nothing issued
+        step(Flag<true>{}, Flag<false>{}, Phase<-1>{}, j, sa, sb);   // no loads left: none issued
         exponentiate(sb, pf);
         pv(vsub(j + 1), pf);
     } else if (j < ntiles) {
