@@ -12,14 +12,18 @@
 // Kernel 2 (dK, dV): one workgroup per (batch, kv-head, 128-key tile); 4 waves x 32 keys.
 //   * The wave's K and V rows stay in registers as MFMA B operands for the whole kernel.
 //   * It walks the q-heads of the kv-head's group and their 64-row query tiles (causal: only
-//     tiles on or below the diagonal).  Q and dO tiles (and the rows' LSE and D) arrive in LDS by
-//     DMA, double-buffered: the next tile streams in while the current one is processed, one
+//     tiles on or below the diagonal; the two of each q-head that meet it come first, in a loop
+//     that applies the mask, and the rest run without mask code, in pairs, with the LDS buffers
+//     as constants).  Q and dO tiles (and the rows' LSE and D) arrive in LDS by DMA,
+//     double-buffered: the next tile streams in while the current one is processed, one
 //     barrier per tile.  The tiles' 16-byte chunks are XOR-swizzled per row so that both the
 //     row reads and the transpose reads are free of bank conflicts without padding.
 //   * S = Q K^T and dP = dO V^T read Q / dO rows as A operands; their C fragments hold one key
 //     per lane, exactly the B-operand layout of dV^T = dO^T P and dK^T = Q^T dS, whose A
 //     operands (one d-column over 8 query rows) come from the same tiles through the LDS
-//     transpose read.  dK and dV accumulate in registers and are written once; with grouped
+//     transpose read.  V is held negated, so that the dP product, started from D, yields
+//     D - dP = -dS / P with no subtraction per score; the sign goes into dK's scale at the
+//     store.  dK and dV accumulate in registers and are written once; with grouped
 //     heads they sum over the group inside the workgroup.
 //   * Keys at or beyond key_lens[b] (and N) read as zeros and are masked out of P, so their dK
 //     and dV come out exactly zero; query rows beyond N read as zeros (Q, dO and their D), so
@@ -34,6 +38,15 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBK = 128;   // keys per workgroup
 constexpr int kBQ = 64;    // query rows per inner tile
+
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
+};
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
 
 template <int D>
 struct BwdCfg {
@@ -71,10 +84,11 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const bf16* __restri
 template <int D>
 struct BwdLds {
     static constexpr int QT = kBQ * D;           // elements of one Q (or dO) tile
-    bf16 q[2][QT];                               // Q tiles, double-buffered
-    bf16 o[2][QT];                               // dO tiles
+    // (statistics first: every LDS address then fits the 16-bit immediate offset of the reads)
     float l2[2][kBQ];                            // base-2 LSE of the tile's rows
     float dd[2][kBQ];                            // D of the tile's rows
+    bf16 q[2][QT];                               // Q tiles, double-buffered
+    bf16 o[2][QT];                               // dO tiles
 };
 
 template <int D, bool CAUSAL>
@@ -131,6 +145,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) kf[s] = vf[s] = bf16x8{};
             }
+            // V is held negated (a sign flip, exact in bf16): the dP product then starts from
+            // D and yields D - dP directly, with no subtraction per score.
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                vf[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, vf[s]) ^ 0x80008000u);
         }
 
         const float Cs = p.scale * kLog2e;
@@ -141,9 +160,25 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
         const size_t Dbase = (size_t)b * p.Hq * N; // row index base of this batch in [B, Hq, N]
         const float* __restrict__ L2 = p.Dsum + (size_t)p.B * p.Hq * N;
 
+        // Tile order: causal first visits, q-head by q-head, the nmo tiles that meet the
+        // workgroup's diagonal, then the remaining tiles of each q-head; a wave needs the mask
+        // only on the first Tm tiles (all of them if its keys reach the key length).
+        static_assert(kBK / kBQ == 2, "diagonal tiles per q-head");
+        const int nmo = CAUSAL ? min(nq, kBK / kBQ) : 0;
+        const int Tm0 = G * nmo;
+        const int Tm = kw0 + 32 > Lk ? T : Tm0;
         auto rowbase = [&](int it, int& i0) {
-            i0 = (qt0 + it % nq) * kBQ;
-            return Dbase + (size_t)(hkv * G + it / nq) * N;
+            int g, t;
+            if (it < Tm0) {
+                g = nmo == 1 ? it : it >> 1;
+                t = it - g * nmo;
+            } else {
+                const int r = it - Tm0, nu = nq - nmo;
+                g = r / nu;
+                t = nmo + r - g * nu;
+            }
+            i0 = (qt0 + t) * kBQ;
+            return Dbase + (size_t)(hkv * G + g) * N;
         };
         // Stage tile `it` (Q, dO rows and their statistics) into buffer `st`.
         auto stage = [&](int it, int st) {
@@ -172,8 +207,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
         wait_vmem();
         __syncthreads();
 
-        for (int it = 0; it < T; ++it) {
-            const int cur = it & 1;
+        // One query tile; the buffer (it & 1) and whether any score of the wave needs the mask
+        // are compile-time, so LDS addresses are constants and unmasked tiles carry no mask code.
+        auto tile = [&](int it, auto cc, auto mm) {
+            constexpr int CC = decltype(cc)::value;   // -1: buffer known at run time
+            const int cur = CC < 0 ? it & 1 : CC;
+            constexpr bool need_mask = decltype(mm)::value;
             int i0;
             (void)rowbase(it, i0);
             if (it + 1 < T) stage(it + 1, cur ^ 1);   // that buffer was released at the last barrier
@@ -192,7 +231,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
             // one scheduling fence per step keeps that order (without it the scheduler sinks
             // each read next to its MFMA and serialises one LDS round trip per MFMA).
             {
-                const bool need_mask = (CAUSAL && kw0 + 31 > i0) || (kw0 + 32 > Lk);
                 // S = Q K^T, dP = dO V^T per half; C row r -> query 32h + 8(r/4) + 4hh + r%4,
                 // column -> key.
                 f32x16 sa[2], pa[2];
@@ -207,29 +245,42 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
                     o_ = trop(Oc + ru, tro[dt][0], tro[dt][1]);
                     q_ = trop(Qc + ru, tro[dt][0], tro[dt][1]);
                 };
-                // Row statistics (LSE2, D) of half h, read from LDS once per half before its
-                // VALU phase (reads inside the phase put LDS latency on the VALU's path).
-                f32x4 l4[4], d4[4];
+                // Base-2 LSE of the rows of half h, read from LDS once per half before its VALU
+                // phase (reads inside the phase put LDS latency on the VALU's path).
+                f32x4 l4[4];
                 auto load_stats = [&](int h) {
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int ql = 32 * h + 8 * g + 4 * hh;
-                        l4[g] = *reinterpret_cast<const f32x4*>(&sm.l2[cur][ql]);
-                        d4[g] = *reinterpret_cast<const f32x4*>(&sm.dd[cur][ql]);
-                    }
+                    for (int g = 0; g < 4; ++g)
+                        l4[g] = *reinterpret_cast<const f32x4*>(&sm.l2[cur][32 * h + 8 * g + 4 * hh]);
                 };
-                // P = 2^(S C - LSE2) and dS = P (dP - D) for scores r0 .. r0 + n - 1 of half h
-                // (the scale of dK is applied at the end).
+                // D of the rows of half h in the C layout: the start value of its dP product.
+                auto d_init = [&](int h) {
+                    f32x16 a;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dd[cur][32 * h + 8 * g + 4 * hh]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) a[4 * g + e] = d4[e];
+                    }
+                    return a;
+                };
+                // P = 2^(S C - LSE2) and -dS = P (D - dP) for scores r0 .. r0 + n - 1 of half h
+                // (the sign and the scale of dK are applied at the end).
+                // Score r of half h belongs to query row i0 + 4 hh + ql(h, r); the causal mask
+                // hides it when the key lies past that row: rel > ql with rel fixed per lane
+                // (and pushed past every ql for keys at or beyond the key length).
+                int rel = 0;
+                if constexpr (need_mask) rel = key >= Lk ? 1 << 30 : key - i0 - 4 * hh;
                 auto softmax_grad = [&](int h, int r0, int n) {
                     for (int r = r0; r < r0 + n; ++r) {
-                        const int ql = 32 * h + 8 * (r >> 2) + 4 * hh + (r & 3);
                         float pv = exp2_hw(__builtin_fmaf(sa[h][r], Cs, -l4[r >> 2][r & 3]));
-                        if (need_mask) {
-                            const bool hide = key >= Lk || (CAUSAL && key > i0 + ql);
+                        if constexpr (need_mask) {
+                            const int ql = 32 * h + 8 * (r >> 2) + (r & 3);
+                            const bool hide = CAUSAL ? rel > ql : key >= Lk;
                             pv = hide ? 0.f : pv;
                         }
                         sa[h][r] = pv;
-                        pa[h][r] = pv * (pa[h][r] - d4[r >> 2][r & 3]);
+                        pa[h][r] = pv * pa[h][r];
                     }
                 };
                 auto to_operands = [&](int h, int uu) {
@@ -246,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
                 for (int h = 0; h < 2; ++h) {
                     if (h == 1) load_stats(0);
                     sa[h] = f32x16{};
-                    pa[h] = f32x16{};
+                    pa[h] = d_init(h);
                     bf16x8 cq, co;
                     rdh(h, 0, cq, co);
 #pragma unroll
@@ -294,11 +345,24 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
             }
             wait_vmem();       // this wave's share of tile it+1 has landed
             __syncthreads();   // tile it+1 visible; buffer `cur` of Q / dO free
+        };
+        // Masked tiles (and an odd start or end of the unmasked run) take the general body;
+        // the unmasked run goes in pairs with the buffers fixed.  The loops are consecutive, not
+        // branches inside one loop: the choice is per wave, and the barriers inside count
+        // waves, not code paths.
+        int it = 0;
+        for (; it < T && (it < Tm || (it & 1)); ++it) tile(it, IntC<-1>{}, Flag<true>{});
+        for (; it + 1 < T; it += 2) {
+            tile(it, IntC<0>{}, Flag<false>{});
+            tile(it + 1, IntC<1>{}, Flag<false>{});
         }
+        if (it < T) tile(it, IntC<-1>{}, Flag<true>{});
     }
 
-    // dK = scale dS^T Q (the scale is applied once here), dV: lane = key, C rows = d.
+    // dK = scale dS^T Q (the scale, and the sign of the -dS products, applied once here), dV:
+    // lane = key, C rows = d.
     if (key < N) {
+        const float ks = -p.scale;
         float* __restrict__ dK = p.dk + kvbase + (size_t)key * D;
         float* __restrict__ dV = p.dv + kvbase + (size_t)key * D;
 #pragma unroll
@@ -306,8 +370,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int dcol = 32 * dt + 8 * g + 4 * hh;
-                float4 kv = {dka[dt][4 * g] * p.scale, dka[dt][4 * g + 1] * p.scale,
-                             dka[dt][4 * g + 2] * p.scale, dka[dt][4 * g + 3] * p.scale};
+                float4 kv = {dka[dt][4 * g] * ks, dka[dt][4 * g + 1] * ks, dka[dt][4 * g + 2] * ks,
+                             dka[dt][4 * g + 3] * ks};
                 float4 vv = {dva[dt][4 * g], dva[dt][4 * g + 1], dva[dt][4 * g + 2], dva[dt][4 * g + 3]};
                 *reinterpret_cast<float4*>(dK + dcol) = kv;
                 *reinterpret_cast<float4*>(dV + dcol) = vv;

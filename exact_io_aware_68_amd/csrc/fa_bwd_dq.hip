@@ -20,8 +20,9 @@
 //   * 64-key K and V tiles are copied global -> LDS by DMA (no staging registers) into
 //     XOR-swizzled tiles, double-buffered: the next tile's copy is issued before the current
 //     tile's MFMAs; one barrier per 64 keys, two 32-key compute steps per tile.
-//   * Causal: key tiles above the diagonal are never loaded; only diagonal and tail tiles are
-//     masked; query tiles run longest first; XCD-aware workgroup order.
+//   * Causal: key tiles above the diagonal are never loaded; the tiles that hide no key run
+//     first without mask code, in pairs with constant LDS buffers, then the diagonal and
+//     key-length tiles with the mask; query tiles run longest first; XCD-aware workgroup order.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -34,6 +35,15 @@ constexpr int kBC = 32;         // keys per compute step
 constexpr int kLT = 64;         // keys per LDS tile
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
+};
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
 
 template <int D>
 struct DqLds {
@@ -124,8 +134,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int x = 0; x < 2; ++x) tro[dt][x] = tr_swz_offset<D>(lane, 32 * dt, x);
 
-    // One 32-key compute step on the half tile at Ks / Vs holding keys k0 ..
-    auto step = [&](const bf16* Ks, const bf16* Vs, int k0) {
+    // One 32-key compute step on the half tile at Ks / Vs holding keys k0 ..; MASK: some key of
+    // the step may lie past this wave's rows or past the key length.
+    auto step = [&](auto mm, const bf16* Ks, const bf16* Vs, int k0) {
+        constexpr bool MASK = decltype(mm)::value;
         // S^T = K Q^T, dP^T = V dO^T: rows = the 32 keys, columns = the wave's queries.
         // Operands of reduction step s+1 are read while the MFMAs of step s run (one fence per
         // step keeps each read from sinking next to its MFMA).
@@ -148,16 +160,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
                 cv = nv;
             }
         }
-        // P and dS (scale applied once at the end); C row r -> key k0 + 8(r/4) + 4hh + r%4.
-        const bool need_mask = (CAUSAL && k0 + kBC - 1 > q0) || (k0 + kBC > Lk);
+        // P and dS (scale applied once at the end); C row r -> key k0 + 4hh + kr(r) with
+        // kr(r) = 8(r/4) + r%4.  The key is hidden when it lies past the row or the key length,
+        // i.e. when kr(r) > thr for one lane constant thr.
+        int thr = Lk - 1 - k0 - 4 * hh;
+        if (CAUSAL) thr = min(thr, qrow - k0 - 4 * hh);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float pv = exp2_hw(__builtin_fmaf(st[r], Cs, -lse2));
-            if (need_mask) {
-                const int key = k0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const bool hide = key >= Lk || (CAUSAL && key > qrow);
-                pv = hide ? 0.f : pv;
-            }
+            if constexpr (MASK) pv = 8 * (r >> 2) + (r & 3) > thr ? 0.f : pv;
             pt[r] = pv * (pt[r] - dd);
         }
         bf16x8 sf[2];
@@ -186,15 +197,28 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
     wait_vmem();
     __syncthreads();
 
-    for (int t = 0; t < ntiles; ++t) {
-        const int cur = t & 1;
+    // One 64-key tile; the buffer is a constant (CC >= 0) or t & 1.
+    auto tile = [&](int t, auto cc, auto mm) {
+        constexpr int CC = decltype(cc)::value;
+        const int cur = CC < 0 ? t & 1 : CC;
         if (t + 1 < ntiles) stage(t + 1, cur ^ 1);   // that buffer was released at the last barrier
         const int k0 = t * kLT;
-        step(sm.k[cur], sm.v[cur], k0);
-        if (k0 + kBC < kend) step(sm.k[cur] + kBC * D, sm.v[cur] + kBC * D, k0 + kBC);
+        step(mm, sm.k[cur], sm.v[cur], k0);
+        if (k0 + kBC < kend) step(mm, sm.k[cur] + kBC * D, sm.v[cur] + kBC * D, k0 + kBC);
         wait_vmem();       // this wave's share of tile t+1 has landed
         __syncthreads();   // tile t+1 visible; buffer cur free
+    };
+    // Tiles below nfree hide no key from any row of the workgroup: they run first, in pairs,
+    // without mask code; the diagonal and key-length tiles follow with the mask.
+    int nfree = Lk / kLT;
+    if (CAUSAL) nfree = min(nfree, (qt * kBR + 1) / kLT);
+    nfree = min(nfree, ntiles);
+    int t = 0;
+    for (; t + 1 < nfree; t += 2) {
+        tile(t, IntC<0>{}, Flag<false>{});
+        tile(t + 1, IntC<1>{}, Flag<false>{});
     }
+    for (; t < ntiles; ++t) tile(t, IntC<-1>{}, Flag<true>{});
 
     // dQ = scale dQ^T^T: lane = query row, C rows = 4 consecutive d per group.
     if (qrow < N) {

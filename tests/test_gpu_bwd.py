@@ -50,6 +50,10 @@ CASES = [  # (B, Hq, Hkv, N, d, causal, padded)
     (1, 2, 2, 1, 128, True, False),
     (1, 2, 2, 65, 128, True, False),
     (1, 1, 1, 513, 128, True, False),
+    # grouped heads with several query tiles per q-head: the diagonal tiles of every q-head
+    # come first, then the rest, with odd and even run lengths
+    (1, 8, 2, 700, 128, True, True),
+    (1, 4, 1, 450, 64, True, False),
 ]
 
 
