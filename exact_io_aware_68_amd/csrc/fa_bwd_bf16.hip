@@ -9,22 +9,27 @@
 //   dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
 //
 // Kernel 1 (prep): per query row, D_i and the base-2 LSE (workspace).
-// Kernel 2 (dK, dV): one workgroup per (batch, kv-head, 128-key tile); 4 waves x 32 keys.
-//   * The wave's K and V rows stay in registers as MFMA B operands for the whole kernel.
+// Kernel 2 (dK, dV): one workgroup per (batch, kv-head, 128-key tile), 8 waves, two per SIMD.
+//   * Wave w takes keys 32 (w & 3) .. + 31 of the tile and the 32-row half w >> 2 of every
+//     64-row query tile: each wave accumulates dK^T, dV^T of its 32 keys (registers) over half
+//     of the rows, and the two halves' partial sums are added through LDS at the end.  The
+//     workgroup's K and V rows sit in LDS for the whole kernel (V negated in place, a sign flip
+//     that is exact in bf16), so a wave fits in 256 registers and two waves share each SIMD.
 //   * It walks the q-heads of the kv-head's group and their 64-row query tiles (causal: only
 //     tiles on or below the diagonal; the two of each q-head that meet it come first, in a loop
 //     that applies the mask, and the rest run without mask code, in pairs, with the LDS buffers
 //     as constants).  Q and dO tiles (and the rows' LSE and D) arrive in LDS by DMA,
 //     double-buffered: the next tile streams in while the current one is processed, one
-//     barrier per tile.  The tiles' 16-byte chunks are XOR-swizzled per row so that both the
-//     row reads and the transpose reads are free of bank conflicts without padding.
-//   * S = Q K^T and dP = dO V^T read Q / dO rows as A operands; their C fragments hold one key
-//     per lane, exactly the B-operand layout of dV^T = dO^T P and dK^T = Q^T dS, whose A
-//     operands (one d-column over 8 query rows) come from the same tiles through the LDS
-//     transpose read.  V is held negated, so that the dP product, started from D, yields
+//     barrier per tile; a cursor advances through the tile order so that the per-tile scalar
+//     work stays small, and only the waves of one query half issue the copies.  The tiles'
+//     16-byte chunks are XOR-swizzled per row so that both the row reads and the transpose
+//     reads are free of bank conflicts without padding.
+//   * S = Q K^T and dP = dO V^T read Q / dO rows as A operands and K / V rows as B operands;
+//     their C fragments hold one key per lane, exactly the B-operand layout of dV^T = dO^T P and
+//     dK^T = Q^T dS, whose A operands (one d-column over 8 query rows) come from the same tiles
+//     through the LDS transpose read.  With V negated the dP product, started from D, yields
 //     D - dP = -dS / P with no subtraction per score; the sign goes into dK's scale at the
-//     store.  dK and dV accumulate in registers and are written once; with grouped
-//     heads they sum over the group inside the workgroup.
+//     store.  With grouped heads dK and dV sum over the group inside the workgroup.
 //   * Keys at or beyond key_lens[b] (and N) read as zeros and are masked out of P, so their dK
 //     and dV come out exactly zero; query rows beyond N read as zeros (Q, dO and their D), so
 //     they contribute nothing.
@@ -81,26 +86,29 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const bf16* __restri
     }
 }
 
+// ---- dK / dV ---------------------------------------------------------------------------
+constexpr int kThreadsKV = 512;
+
 template <int D>
 struct BwdLds {
-    static constexpr int QT = kBQ * D;           // elements of one Q (or dO) tile
-    // (statistics first: every LDS address then fits the 16-bit immediate offset of the reads)
-    float l2[2][kBQ];                            // base-2 LSE of the tile's rows
-    float dd[2][kBQ];                            // D of the tile's rows
-    bf16 q[2][QT];                               // Q tiles, double-buffered
-    bf16 o[2][QT];                               // dO tiles
+    static constexpr int QT = kBQ * D;
+    float l2[2][kBQ];   // base-2 LSE of the tile's rows
+    float dd[2][kBQ];   // D of the tile's rows
+    bf16 q[2][QT];      // Q tiles, double-buffered
+    bf16 o[2][QT];      // dO tiles
+    bf16 k[kBK * D];    // the workgroup's K rows
+    bf16 v[kBK * D];    // its V rows, negated
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreadsKV) void bwd_dkdv_kernel(BwdParams p) {
     using C = BwdCfg<D>;
     constexpr int NS = C::NS, ND = C::ND;
     __shared__ __attribute__((aligned(1024))) BwdLds<D> sm;
 
     const int tid = threadIdx.x;
-    // The wave index is uniform across the wave; saying so keeps buffer resources and DMA
-    // addresses derived from it in scalar registers.
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = w & 3, hq = w >> 2;                // key group, query half
     const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
     const int N = p.N;
     const int nkt = (N + kBK - 1) / kBK;
@@ -110,15 +118,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
     const int b = head / p.Hkv, hkv = head - b * p.Hkv;
     const int G = p.Hq / p.Hkv;
     const int k0 = kt * kBK;
-    const int kw0 = k0 + 32 * w;                      // this wave's first key
+    const int kw0 = k0 + 32 * kg;                     // this wave's first key
     const int key = kw0 + c;                          // this lane's key
 
     int Lk = N;
     if (p.key_lens) Lk = min(max(p.key_lens[b], 0), N);
 
     const size_t kvbase = (size_t)(b * p.Hkv + hkv) * N * D;
-    const bf16* __restrict__ K = (const bf16*)p.k + kvbase;
-    const bf16* __restrict__ V = (const bf16*)p.v + kvbase;
 
     f32x16 dka[ND], dva[ND];
 #pragma unroll
@@ -127,31 +133,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
         dva[i] = f32x16{};
     }
 
-    if (k0 < Lk) {
-        // K, V rows of this lane's key: B operands of S and dP (slots = 8 consecutive d); keys
-        // at or beyond Lk read as zeros.
-        bf16x8 kf[NS], vf[NS];
-        {
-            const uint32_t nb = (uint32_t)min(Lk - kw0, 32) * D * 2;
-            if (kw0 < Lk) {
-                const rsrc_t rk = make_rsrc(K + (size_t)kw0 * D, nb);
-                const rsrc_t rv = make_rsrc(V + (size_t)kw0 * D, nb);
-#pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    kf[s] = __builtin_bit_cast(bf16x8, buf_ld16(rk, (c * D + 16 * s + 8 * hh) * 2));
-                    vf[s] = __builtin_bit_cast(bf16x8, buf_ld16(rv, (c * D + 16 * s + 8 * hh) * 2));
-                }
-            } else {
-#pragma unroll
-                for (int s = 0; s < NS; ++s) kf[s] = vf[s] = bf16x8{};
-            }
-            // V is held negated (a sign flip, exact in bf16): the dP product then starts from
-            // D and yields D - dP directly, with no subtraction per score.
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-                vf[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, vf[s]) ^ 0x80008000u);
-        }
-
+    if (k0 < Lk) {   // (uniform over the workgroup)
         const float Cs = p.scale * kLog2e;
         const int nqt = (N + kBQ - 1) / kBQ;
         const int qt0 = CAUSAL ? k0 / kBQ : 0;
@@ -167,34 +149,63 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
         const int nmo = CAUSAL ? min(nq, kBK / kBQ) : 0;
         const int Tm0 = G * nmo;
         const int Tm = kw0 + 32 > Lk ? T : Tm0;
-        auto rowbase = [&](int it, int& i0) {
-            int g, t;
-            if (it < Tm0) {
-                g = nmo == 1 ? it : it >> 1;
-                t = it - g * nmo;
-            } else {
-                const int r = it - Tm0, nu = nq - nmo;
-                g = r / nu;
-                t = nmo + r - g * nu;
+        // Staging cursor over that order (q-head cg, tile ct, row base crb of the q-head),
+        // advanced by one tile per stage: no division and little scalar work per tile, which
+        // all eight waves would otherwise repeat on the CU's one scalar unit after each barrier.
+        const size_t rb0 = Dbase + (size_t)(hkv * G) * N;
+        int cg = 0, ct = 0;
+        size_t crb = rb0;
+        int i0_next = 0;   // first row of the tile staged last
+        // Stage the cursor's tile into buffer st and advance; the waves of query half 0 issue
+        // the copies, so those of half 1 skip this work.
+        auto stage = [&](int st) {
+            const int i0 = (qt0 + ct) * kBQ;
+            i0_next = i0;
+            if (hq == 0) {
+                const size_t r = crb + i0;
+                dma_tile<D, kBQ, kThreadsKV / 128>((const bf16*)p.q + r * D, N - i0, sm.q[st], w, lane);
+                dma_tile<D, kBQ, kThreadsKV / 128>((const bf16*)p.dO + r * D, N - i0, sm.o[st], w, lane);
+                const uint32_t nb = (uint32_t)min(N - i0, kBQ) * 4;
+                if (w == 0) dma4(make_rsrc(L2 + r, nb), lane * 4, sm.l2[st]);
+                if (w == 1) dma4(make_rsrc(p.Dsum + r, nb), lane * 4, sm.dd[st]);
             }
-            i0 = (qt0 + t) * kBQ;
-            return Dbase + (size_t)(hkv * G + g) * N;
-        };
-        // Stage tile `it` (Q, dO rows and their statistics) into buffer `st`.
-        auto stage = [&](int it, int st) {
-            int i0;
-            const size_t rb = rowbase(it, i0);
-            dma_tile<D, kBQ, kThreads / 64>((const bf16*)p.q + (rb + i0) * D, N - i0, sm.q[st], w, lane);
-            dma_tile<D, kBQ, kThreads / 64>((const bf16*)p.dO + (rb + i0) * D, N - i0, sm.o[st], w, lane);
-            const uint32_t nb = (uint32_t)min(N - i0, kBQ) * 4;
-            if (w == 0) dma4(make_rsrc(L2 + rb + i0, nb), lane * 4, sm.l2[st]);
-            if (w == 1) dma4(make_rsrc(p.Dsum + rb + i0, nb), lane * 4, sm.dd[st]);
+            if (ct < nmo) {   // diagonal segment: (q-head, tile < nmo), tile fastest
+                if (++ct == nmo) {
+                    ct = 0;
+                    crb += N;
+                    if (++cg == G) {   // on to the remaining tiles, from the first q-head
+                        cg = 0;
+                        ct = nmo;
+                        crb = rb0;
+                    }
+                }
+            } else if (++ct == nq) {
+                ct = nmo;
+                ++cg;
+                crb += N;
+            }
         };
 
-        // Per-lane LDS offsets.  Row reads of Q / dO rows 32 q2 + c, chunk 2s + hh:
-        int qro[NS];
+        // K and V rows of the workgroup (keys at or beyond Lk arrive as zeros), then tile 0.
+        dma_tile<D, kBK, kThreadsKV / 64>((const bf16*)p.k + kvbase + (size_t)k0 * D, Lk - k0, sm.k, w, lane);
+        dma_tile<D, kBK, kThreadsKV / 64>((const bf16*)p.v + kvbase + (size_t)k0 * D, Lk - k0, sm.v, w, lane);
+        stage(0);
+        wait_vmem();
+        __syncthreads();
+        // V negated in place (a sign flip, exact in bf16): the dP product started from D then
+        // yields D - dP = -dS / P with no subtraction per score.
+        {
+            constexpr int NV = kBK * D * 2 / 16 / kThreadsKV;
+            u32x4* vv = reinterpret_cast<u32x4*>(sm.v);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) qro[s] = swz_at<D>(c, 16 * s + 8 * hh);
+            for (int i = 0; i < NV; ++i) vv[tid + kThreadsKV * i] ^= 0x80008000u;
+        }
+        __syncthreads();
+
+        // Per-lane LDS offsets.  Row reads (Q / dO rows and K / V rows c, chunk 2s + hh):
+        int ro[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) ro[s] = swz_at<D>(c, 16 * s + 8 * hh);
         // transpose reads of dO^T / Q^T (columns 32 dt): rows 16u + ...
         int tro[ND][2];
 #pragma unroll
@@ -202,154 +213,90 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
             for (int x = 0; x < 2; ++x) tro[dt][x] = tr_swz_offset<D>(lane, 32 * dt, x);
         auto trop = [](const bf16* base, int o0, int o1) { return join(lds_tr(base + o0), lds_tr(base + o1)); };
+        const bf16* Kw = sm.k + 32 * kg * D;
+        const bf16* Vw = sm.v + 32 * kg * D;
 
-        stage(0, 0);
-        wait_vmem();
-        __syncthreads();
-
-        // One query tile; the buffer (it & 1) and whether any score of the wave needs the mask
-        // are compile-time, so LDS addresses are constants and unmasked tiles carry no mask code.
         auto tile = [&](int it, auto cc, auto mm) {
             constexpr int CC = decltype(cc)::value;   // -1: buffer known at run time
             const int cur = CC < 0 ? it & 1 : CC;
             constexpr bool need_mask = decltype(mm)::value;
-            int i0;
-            (void)rowbase(it, i0);
-            if (it + 1 < T) stage(it + 1, cur ^ 1);   // that buffer was released at the last barrier
-            const bf16* Qc = sm.q[cur];
-            const bf16* Oc = sm.o[cur];
-
-            // Waves whose keys all lie above the diagonal of this tile (only on a workgroup's
-            // first query tile) run it anyway: the causal mask makes P = 0, so dS = 0 and the
-            // accumulators are unchanged; a branch here would cost more in register copies.
-            //
-            // The tile's 64 query rows are two 32-row halves h, and the products run in four
-            // phases so that the VALU work of one half runs alongside MFMAs of the other:
-            //   A: S, dP of half 0;   B: S, dP of half 1      + P, dS of half 0 (VALU);
-            //   C: dV, dK of half 0   + P, dS of half 1 (VALU);   D: dV, dK of half 1.
-            // Within a phase the LDS operands of MFMA step k+1 are read while step k runs, and
-            // one scheduling fence per step keeps that order (without it the scheduler sinks
-            // each read next to its MFMA and serialises one LDS round trip per MFMA).
-            {
-                // S = Q K^T, dP = dO V^T per half; C row r -> query 32h + 8(r/4) + 4hh + r%4,
-                // column -> key.
-                f32x16 sa[2], pa[2];
-                bf16x8 pf[4], sf[4];   // B operands of dV, dK for query groups u = 2h + 0/1
-                auto rdh = [&](int h, int k, bf16x8& q_, bf16x8& o_) {   // A operands, step k
-                    const int ro = 32 * h * D + qro[k];
-                    q_ = __builtin_bit_cast(bf16x8, ld16(Qc + ro));
-                    o_ = __builtin_bit_cast(bf16x8, ld16(Oc + ro));
-                };
-                auto rdt = [&](int h, int g, bf16x8& o_, bf16x8& q_) {   // dO^T, Q^T, step g
-                    const int dt = g >> 1, ru = 16 * (2 * h + (g & 1)) * D;
-                    o_ = trop(Oc + ru, tro[dt][0], tro[dt][1]);
-                    q_ = trop(Qc + ru, tro[dt][0], tro[dt][1]);
-                };
-                // Base-2 LSE of the rows of half h, read from LDS once per half before its VALU
-                // phase (reads inside the phase put LDS latency on the VALU's path).
-                f32x4 l4[4];
-                auto load_stats = [&](int h) {
+            const int i0 = i0_next;                  // (staged one tile ago)
+            if (it + 1 < T) stage(cur ^ 1);          // that buffer was released at the last barrier
+            const bf16* Qc = sm.q[cur] + 32 * hq * D;
+            const bf16* Oc = sm.o[cur] + 32 * hq * D;
+            // S = Q K^T and D - dP (C row r -> query 8(r/4) + 4hh + r%4 of the half, column ->
+            // key), operands read one step ahead.
+            f32x16 sa = f32x16{}, pa;
 #pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        l4[g] = *reinterpret_cast<const f32x4*>(&sm.l2[cur][32 * h + 8 * g + 4 * hh]);
-                };
-                // D of the rows of half h in the C layout: the start value of its dP product.
-                auto d_init = [&](int h) {
-                    f32x16 a;
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dd[cur][32 * hq + 8 * g + 4 * hh]);
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dd[cur][32 * h + 8 * g + 4 * hh]);
+                for (int e = 0; e < 4; ++e) pa[4 * g + e] = d4[e];
+            }
+            // The S chain, then the dP chain (each MFMA accumulates onto the previous one's
+            // result; the other wave on the SIMD fills the gaps).
+            auto rds = [&](int s, bf16x8 (&x)[2]) {
+                const int k = s % NS;
+                x[0] = __builtin_bit_cast(bf16x8, ld16((s < NS ? Qc : Oc) + ro[k]));
+                x[1] = __builtin_bit_cast(bf16x8, ld16((s < NS ? Kw : Vw) + ro[k]));
+            };
+            bf16x8 op[2][2];
+            rds(0, op[0]);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) a[4 * g + e] = d4[e];
-                    }
-                    return a;
-                };
-                // P = 2^(S C - LSE2) and -dS = P (D - dP) for scores r0 .. r0 + n - 1 of half h
-                // (the sign and the scale of dK are applied at the end).
-                // Score r of half h belongs to query row i0 + 4 hh + ql(h, r); the causal mask
-                // hides it when the key lies past that row: rel > ql with rel fixed per lane
-                // (and pushed past every ql for keys at or beyond the key length).
-                int rel = 0;
-                if constexpr (need_mask) rel = key >= Lk ? 1 << 30 : key - i0 - 4 * hh;
-                auto softmax_grad = [&](int h, int r0, int n) {
-                    for (int r = r0; r < r0 + n; ++r) {
-                        float pv = exp2_hw(__builtin_fmaf(sa[h][r], Cs, -l4[r >> 2][r & 3]));
-                        if constexpr (need_mask) {
-                            const int ql = 32 * h + 8 * (r >> 2) + (r & 3);
-                            const bool hide = CAUSAL ? rel > ql : key >= Lk;
-                            pv = hide ? 0.f : pv;
-                        }
-                        sa[h][r] = pv;
-                        pa[h][r] = pv * pa[h][r];
-                    }
-                };
-                auto to_operands = [&](int h, int uu) {
-                    const int u = 2 * h + uu, o8 = 8 * uu;
-                    pf[u] = to_bf16x8(sa[h][o8], sa[h][o8 + 1], sa[h][o8 + 2], sa[h][o8 + 3],
-                                      sa[h][o8 + 4], sa[h][o8 + 5], sa[h][o8 + 6], sa[h][o8 + 7]);
-                    sf[u] = to_bf16x8(pa[h][o8], pa[h][o8 + 1], pa[h][o8 + 2], pa[h][o8 + 3],
-                                      pa[h][o8 + 4], pa[h][o8 + 5], pa[h][o8 + 6], pa[h][o8 + 7]);
-                };
-                constexpr int EB = 16 / NS;         // scores per S/dP step of phase B
-                constexpr int EC = 16 / (2 * ND);   // scores per dV/dK step of phase C
-                // Phases A and B: S, dP of half h (MFMA), with half 0's softmax gradient in B.
+            for (int s = 0; s < 2 * NS; ++s) {
+                if (s + 1 < 2 * NS) rds(s + 1, op[(s + 1) & 1]);
+                if (s < NS) sa = mfma32(op[s & 1][0], op[s & 1][1], sa);
+                else pa = mfma32(op[s & 1][0], op[s & 1][1], pa);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // P = 2^(S C - LSE2) and -dS = P (D - dP); the causal mask hides score r when the
+            // key lies past its row: rel > 8(r/4) + r%4 with rel fixed per lane (and pushed past
+            // every row for keys at or beyond the key length).
+            f32x4 l4[4];
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    if (h == 1) load_stats(0);
-                    sa[h] = f32x16{};
-                    pa[h] = d_init(h);
-                    bf16x8 cq, co;
-                    rdh(h, 0, cq, co);
+            for (int g = 0; g < 4; ++g)
+                l4[g] = *reinterpret_cast<const f32x4*>(&sm.l2[cur][32 * hq + 8 * g + 4 * hh]);
+            int rel = 0;
+            if constexpr (need_mask) rel = key >= Lk ? 1 << 30 : key - i0 - 32 * hq - 4 * hh;
 #pragma unroll
-                    for (int k = 0; k < NS; ++k) {
-                        bf16x8 nq, no;
-                        if (k + 1 < NS) rdh(h, k + 1, nq, no);
-                        sa[h] = mfma32(cq, kf[k], sa[h]);
-                        pa[h] = mfma32(co, vf[k], pa[h]);
-                        if (h == 1) {
-                            softmax_grad(0, EB * k, EB);
-                            if ((EB * (k + 1)) % 8 == 0) to_operands(0, EB * (k + 1) / 8 - 1);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                        if (k + 1 < NS) {
-                            cq = nq;
-                            co = no;
-                        }
-                    }
+            for (int r = 0; r < 16; ++r) {
+                float pv = exp2_hw(__builtin_fmaf(sa[r], Cs, -l4[r >> 2][r & 3]));
+                if constexpr (need_mask) {
+                    const bool hide = CAUSAL ? rel > 8 * (r >> 2) + (r & 3) : key >= Lk;
+                    pv = hide ? 0.f : pv;
                 }
-                // Phases C and D: dV^T += dO^T P, dK^T += Q^T dS of half h (A = one d-column
-                // over 8 query rows), with half 1's softmax gradient in C.
+                sa[r] = pv;
+                pa[r] = pv * pa[r];
+            }
+            bf16x8 pf[2], sf[2];   // B operands of dV, dK: query rows 16u + ...
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    if (h == 0) load_stats(1);
-                    bf16x8 ao, aq;
-                    rdt(h, 0, ao, aq);
+            for (int u = 0; u < 2; ++u) {
+                const int o8 = 8 * u;
+                pf[u] = to_bf16x8(sa[o8], sa[o8 + 1], sa[o8 + 2], sa[o8 + 3], sa[o8 + 4], sa[o8 + 5],
+                                  sa[o8 + 6], sa[o8 + 7]);
+                sf[u] = to_bf16x8(pa[o8], pa[o8 + 1], pa[o8 + 2], pa[o8 + 3], pa[o8 + 4], pa[o8 + 5],
+                                  pa[o8 + 6], pa[o8 + 7]);
+            }
+            // dV^T += dO^T P, dK^T += Q^T (-dS): A = one d-column over 8 query rows (transpose
+            // reads), read one step ahead.
+            auto rdt = [&](int g, bf16x8 (&x)[2]) {
+                const int dt = g >> 1, ru = 16 * (g & 1) * D;
+                x[0] = trop(Oc + ru, tro[dt][0], tro[dt][1]);
+                x[1] = trop(Qc + ru, tro[dt][0], tro[dt][1]);
+            };
+            bf16x8 ot[2][2];
+            rdt(0, ot[0]);
 #pragma unroll
-                    for (int g = 0; g < 2 * ND; ++g) {
-                        bf16x8 no, nq;
-                        if (g + 1 < 2 * ND) rdt(h, g + 1, no, nq);
-                        const int dt = g >> 1, u = 2 * h + (g & 1);
-                        dva[dt] = mfma32(ao, pf[u], dva[dt]);
-                        dka[dt] = mfma32(aq, sf[u], dka[dt]);
-                        if (h == 0) {
-                            softmax_grad(1, EC * g, EC);
-                            if ((EC * (g + 1)) % 8 == 0) to_operands(1, EC * (g + 1) / 8 - 1);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                        if (g + 1 < 2 * ND) {
-                            ao = no;
-                            aq = nq;
-                        }
-                    }
-                }
+            for (int g = 0; g < 2 * ND; ++g) {
+                if (g + 1 < 2 * ND) rdt(g + 1, ot[(g + 1) & 1]);
+                const int dt = g >> 1, u = g & 1;
+                dva[dt] = mfma32(ot[g & 1][0], pf[u], dva[dt]);
+                dka[dt] = mfma32(ot[g & 1][1], sf[u], dka[dt]);
+                __builtin_amdgcn_sched_barrier(0);
             }
             wait_vmem();       // this wave's share of tile it+1 has landed
             __syncthreads();   // tile it+1 visible; buffer `cur` of Q / dO free
         };
-        // Masked tiles (and an odd start or end of the unmasked run) take the general body;
-        // the unmasked run goes in pairs with the buffers fixed.  The loops are consecutive, not
-        // branches inside one loop: the choice is per wave, and the barriers inside count
-        // waves, not code paths.
         int it = 0;
         for (; it < T && (it < Tm || (it & 1)); ++it) tile(it, IntC<-1>{}, Flag<true>{});
         for (; it + 1 < T; it += 2) {
@@ -359,22 +306,33 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdParams p) {
         if (it < T) tile(it, IntC<-1>{}, Flag<true>{});
     }
 
-    // dK = scale dS^T Q (the scale, and the sign of the -dS products, applied once here), dV:
-    // lane = key, C rows = d.
+    // The two query halves' partial sums meet in LDS (the tiles are dead after the last
+    // barrier): half 0 hands over its dV, half 1 its dK; half 0 then stores dK, half 1 dV.
+    // Layout: one f32x4 per lane per (dt, g), lanes consecutive.
+    static_assert(sizeof(BwdLds<D>) - 2 * 2 * kBQ * 4 >= 4 * 2 * ND * 4 * 64 * 16, "exchange fits");
+    f32x4* xb = reinterpret_cast<f32x4*>(&sm.q[0][0]);
+    auto slot = [&](int kind, int dt, int g) { return ((kg * 2 + kind) * ND * 4 + dt * 4 + g) * 64 + lane; };
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x16& a = hq == 0 ? dva[dt] : dka[dt];
+            xb[slot(hq == 0 ? 1 : 0, dt, g)] = f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+        }
+    __syncthreads();
     if (key < N) {
-        const float ks = -p.scale;
-        float* __restrict__ dK = p.dk + kvbase + (size_t)key * D;
-        float* __restrict__ dV = p.dv + kvbase + (size_t)key * D;
+        // dK = scale dS^T Q (scale and the sign of the -dS products applied here); lane = key.
+        const float sc = hq == 0 ? -p.scale : 1.f;
+        float* __restrict__ dst = (hq == 0 ? p.dk : p.dv) + kvbase + (size_t)key * D;
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int dcol = 32 * dt + 8 * g + 4 * hh;
-                float4 kv = {dka[dt][4 * g] * ks, dka[dt][4 * g + 1] * ks, dka[dt][4 * g + 2] * ks,
-                             dka[dt][4 * g + 3] * ks};
-                float4 vv = {dva[dt][4 * g], dva[dt][4 * g + 1], dva[dt][4 * g + 2], dva[dt][4 * g + 3]};
-                *reinterpret_cast<float4*>(dK + dcol) = kv;
-                *reinterpret_cast<float4*>(dV + dcol) = vv;
+                const f32x16& a = hq == 0 ? dka[dt] : dva[dt];
+                const f32x4 x = xb[slot(hq == 0 ? 0 : 1, dt, g)];
+                const float4 v = {(a[4 * g] + x[0]) * sc, (a[4 * g + 1] + x[1]) * sc,
+                                  (a[4 * g + 2] + x[2]) * sc, (a[4 * g + 3] + x[3]) * sc};
+                *reinterpret_cast<float4*>(dst + 32 * dt + 8 * g + 4 * hh) = v;
             }
     }
 }
@@ -396,7 +354,7 @@ hipError_t launch_bwd_prep_bf16(const BwdParams& p, hipStream_t stream) {
 
 hipError_t launch_bwd_dkdv_bf16(const BwdParams& p, hipStream_t stream) {
     const int nkt = (p.N + kBK - 1) / kBK;
-    dim3 grid((unsigned)(nkt * p.Hkv * p.B)), block(kThreads);
+    dim3 grid((unsigned)(nkt * p.Hkv * p.B)), block(kThreadsKV);
     if (p.d == 128) {
         if (p.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), grid, block, 0, stream, p);
