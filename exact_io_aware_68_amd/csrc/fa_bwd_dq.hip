@@ -87,7 +87,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
     const float Cs = p.scale * kLog2e;
 
     // Q and dO fragments: B operands (lane = query row, slots = 8 consecutive d).  Rows past N
-    // read as zeros; their LSE2 is +inf so P = 0 there.
+    // read as zeros; their LSE2 is +inf so P = 0 there.  dO is held negated (a sign flip, exact
+    // in bf16), so that the dP^T product started from D yields D - dP = -dS / P with no
+    // subtraction per score; the sign goes into dQ's scale at the store.
     bf16x8 qf[NS], of[NS];
     float lse2 = kPosInf, dd = 0.f;
     {
@@ -100,13 +102,16 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
                 g = ld16(dO + (size_t)qrow * D + 16 * s + 8 * hh);
             }
             qf[s] = __builtin_bit_cast(bf16x8, a);
-            of[s] = __builtin_bit_cast(bf16x8, g);
+            of[s] = __builtin_bit_cast(bf16x8, g ^ 0x80008000u);
         }
         if (qrow < N) {
             dd = p.Dsum[qrow0 + qrow];
             lse2 = p.Dsum[(size_t)p.B * p.Hq * N + qrow0 + qrow];
         }
     }
+    f32x16 dvec;   // start value of every dP^T product: the row's D in all 16 C entries
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dvec[r] = dd;
 
     int kend = Lk;
     if (CAUSAL) kend = min(kend, qt * kBR + kBR);
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
         // S^T = K Q^T, dP^T = V dO^T: rows = the 32 keys, columns = the wave's queries.
         // Operands of reduction step s+1 are read while the MFMAs of step s run (one fence per
         // step keeps each read from sinking next to its MFMA).
-        f32x16 st = f32x16{}, pt = f32x16{};
+        f32x16 st = f32x16{}, pt = dvec;
         bf16x8 ck, cv;
         auto rd = [&](int s, bf16x8& k_, bf16x8& v_) {
             k_ = __builtin_bit_cast(bf16x8, ld16(Ks + kro[s]));
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
         for (int r = 0; r < 16; ++r) {
             float pv = exp2_hw(__builtin_fmaf(st[r], Cs, -lse2));
             if constexpr (MASK) pv = 8 * (r >> 2) + (r & 3) > thr ? 0.f : pv;
-            pt[r] = pv * (pt[r] - dd);
+            pt[r] = pv * pt[r];   // -dS
         }
         bf16x8 sf[2];
 #pragma unroll
@@ -220,15 +225,17 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
     }
     for (; t < ntiles; ++t) tile(t, IntC<-1>{}, Flag<true>{});
 
-    // dQ = scale dQ^T^T: lane = query row, C rows = 4 consecutive d per group.
+    // dQ = scale dS K = -scale (the accumulated -dS K): lane = query row, C rows = 4 consecutive
+    // d per group.
     if (qrow < N) {
+        const float ns = -p.scale;
         float* dst = p.dq + (qrow0 + qrow) * D;
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float4 v = {acc[dt][4 * g] * p.scale, acc[dt][4 * g + 1] * p.scale,
-                                  acc[dt][4 * g + 2] * p.scale, acc[dt][4 * g + 3] * p.scale};
+                const float4 v = {acc[dt][4 * g] * ns, acc[dt][4 * g + 1] * ns,
+                                  acc[dt][4 * g + 2] * ns, acc[dt][4 * g + 3] * ns};
                 *reinterpret_cast<float4*>(dst + 32 * dt + 8 * g + 4 * hh) = v;
             }
     }
