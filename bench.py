@@ -319,7 +319,7 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 TRAFFIC_CMD = """    cd /tmp && export TMPDIR=/tmp
     for C in FETCH_SIZE WRITE_SIZE; do
       rocprofv3 --pmc $C -T -f csv -d $REPO/gpurun_out/pmc -o bench_$C -- \\
-          python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline
+          python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline --cold-steps 0
       rocprofv3 --pmc $C -T -f csv -d $REPO/gpurun_out/pmc -o copy_$C -- \\
           python3 $REPO/bench.py --copy-calib
     done
@@ -560,6 +560,9 @@ def main():
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--only", choices=["fwd", "bwd", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=3,
+                    help="steps timed kernel by kernel after a 512 MiB cache-evicting read "
+                         "(reported as kernels_ms_cold_cache; 0 for profiling runs)")
     ap.add_argument("--splits", type=int, default=0,
                     help="decode workloads: number of key ranges (0: the library's choice)")
     ap.add_argument("--copy-calib", action="store_true")
@@ -618,25 +621,36 @@ def main():
     names = (["fwd_bf16"] if do_fwd else []) + (["bwd_prep", "bwd_dkdv", "bwd_dq"] if do_bwd else [])
     ev = {n: [] for n in names}
 
-    def step(record):
-        def mark(n, fn):
+    fns = {"fwd_bf16": lambda: fa.fa_fwd(q, k, v, scale=sc, causal=causal, key_lens=kl, o=o, lse=lse),
+           "bwd_prep": lambda: fa.fa_bwd_prep(o, do, lse, ws),
+           "bwd_dkdv": lambda: fa.fa_bwd_dkdv(q, k, v, do, dk, dv, ws, scale=sc, causal=causal,
+                                              key_lens=kl),
+           "bwd_dq": lambda: fa.fa_bwd_dq(q, k, v, do, dq, ws, scale=sc, causal=causal, key_lens=kl)}
+
+    def step(record, flush=None, store=None):
+        for n in names:
+            if flush is not None:   # evict L2 and the Infinity Cache, outside the events
+                torch.sum(flush[0], dim=0, out=flush[1])
             if record:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                fn()
+                fns[n]()
                 e1.record(stream)
-                ev[n].append((e0, e1))
+                (ev if store is None else store)[n].append((e0, e1))
             else:
-                fn()
-        if do_fwd:
-            mark("fwd_bf16", lambda: fa.fa_fwd(q, k, v, scale=sc, causal=causal, key_lens=kl,
-                                               o=o, lse=lse))
-        if do_bwd:
-            mark("bwd_prep", lambda: fa.fa_bwd_prep(o, do, lse, ws))
-            mark("bwd_dkdv", lambda: fa.fa_bwd_dkdv(q, k, v, do, dk, dv, ws, scale=sc,
-                                                    causal=causal, key_lens=kl))
-            mark("bwd_dq", lambda: fa.fa_bwd_dq(q, k, v, do, dq, ws, scale=sc, causal=causal,
-                                                key_lens=kl))
+                fns[n]()
+
+    # Per-kernel times with cold caches: each launch follows a 512 MiB read (run first, so the
+    # last dispatches of a traced run are the timed steps below).
+    cold = {n: [] for n in names}
+    if args.cold_steps > 0:
+        fl = (torch.ones(128 << 20, dtype=torch.float32, device=dev),
+              torch.empty((), dtype=torch.float32, device=dev))
+        step(False)
+        for _ in range(args.cold_steps):
+            step(True, flush=fl, store=cold)
+        torch.cuda.synchronize()
+        del fl
 
     for _ in range(args.warmup):
         step(False)
@@ -685,6 +699,8 @@ def main():
                    "seed": w.seed, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {n: round(t, 4) for n, t in kern_ms.items()},
+        "kernels_ms_cold_cache": None if args.cold_steps <= 0 else {
+            n: round(sum(a.elapsed_time(b) for a, b in cold[n]) / len(cold[n]), 4) for n in names},
         "fwd": None if not do_fwd else {
             "tflops": round(ff / (kern_ms["fwd_bf16"] * 1e-3) / 1e12, 2),
             "pct_peak": round(100 * ff / (kern_ms["fwd_bf16"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
