@@ -563,6 +563,7 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=3,
                     help="steps timed kernel by kernel after a 512 MiB cache-evicting read "
                          "(reported as kernels_ms_cold_cache; 0 for profiling runs)")
+    ap.add_argument("--flush-mib", type=int, default=512, help=argparse.SUPPRESS)
     ap.add_argument("--splits", type=int, default=0,
                     help="decode workloads: number of key ranges (0: the library's choice)")
     ap.add_argument("--copy-calib", action="store_true")
@@ -628,6 +629,10 @@ def main():
            "bwd_dq": lambda: fa.fa_bwd_dq(q, k, v, do, dq, ws, scale=sc, causal=causal, key_lens=kl)}
 
     def step(record, flush=None, store=None):
+        if flush is not None:
+            # a spin of a few ms first, so that the host has queued the whole step (flushes,
+            # events, kernels) before the GPU reaches it: no launch gap inside an event pair
+            torch.cuda._sleep(5_000_000)
         for n in names:
             if flush is not None:   # evict L2 and the Infinity Cache, outside the events
                 torch.sum(flush[0], dim=0, out=flush[1])
@@ -640,18 +645,6 @@ def main():
             else:
                 fns[n]()
 
-    # Per-kernel times with cold caches: each launch follows a 512 MiB read (run first, so the
-    # last dispatches of a traced run are the timed steps below).
-    cold = {n: [] for n in names}
-    if args.cold_steps > 0:
-        fl = (torch.ones(128 << 20, dtype=torch.float32, device=dev),
-              torch.empty((), dtype=torch.float32, device=dev))
-        step(False)
-        for _ in range(args.cold_steps):
-            step(True, flush=fl, store=cold)
-        torch.cuda.synchronize()
-        del fl
-
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
@@ -662,6 +655,17 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     kern_ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in names}
+    # Per-kernel times with cold caches: each launch follows a 512 MiB read that evicts L2 and
+    # the Infinity Cache (after the timed steps, with the clocks already up; profiling runs pass
+    # --cold-steps 0, so their last dispatches are the timed steps).
+    cold = {n: [] for n in names}
+    if args.cold_steps > 0:
+        fl = (torch.ones(args.flush_mib << 18, dtype=torch.float32, device=dev),
+              torch.empty((), dtype=torch.float32, device=dev))
+        for _ in range(args.cold_steps):
+            step(True, flush=fl, store=cold)
+        torch.cuda.synchronize()
+        del fl
 
     ff = fwd_flops(w.B, w.Hq, w.N, w.d, causal) if do_fwd else 0.0
     bf = bwd_flops(w.B, w.Hq, w.N, w.d, causal) if do_bwd else 0.0
