@@ -340,9 +340,27 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
     };
     int j = 0;   // stays even: pairs of steps share one LDS tile
     if constexpr (WIN) {
-        // Window edges cut steps at both ends of the range; every step applies the mask (a
-        // per-pair choice between masked and unmasked bodies measured slower: the two bodies
-        // pushed the kernel past the register file).
+        // Window edges cut steps at both ends of this wave's range: steps below jlo meet the
+        // left edge, steps from jhi on the right edge or the key length; the steps between
+        // hide no key from any row of the wave and run without mask code.  Three consecutive
+        // loops, not a choice inside one loop (that pushed the kernel past the register file);
+        // every wave still runs every step, so the barriers inside match.
+        static_assert(!CAUSAL, "a causal window is the window (wl, 0)");
+        int jlo = 0, jhi = 1 << 30;
+        if (wl >= 0) jlo = max(0, (q0 + kWR - 1 - wl - kb + kBC - 1) / kBC);
+        if (wr >= 0) {
+            const int R = q0 + wr - (kBC - 1) - kb;   // step j is cut iff 32 j > R
+            jhi = R < 0 ? 0 : R / kBC + 1;
+        }
+        jhi = min(jhi, max(Lr, 0) / kBC);              // step j reaches Lk iff 32 j + 32 > Lr
+        for (; j + 2 < ntiles && j + 1 < jlo; j += 2) {
+            step(Flag<true>{}, Flag<false>{}, Phase<-1>{}, j, sa, sb);
+            step(Flag<true>{}, Flag<true>{}, Phase<-1>{}, j + 1, sb, sa);
+        }
+        for (; j + 2 < ntiles && j + 2 < jhi; j += 2) {
+            step(Flag<false>{}, Flag<false>{}, Phase<-1>{}, j, sa, sb);
+            step(Flag<false>{}, Flag<true>{}, Phase<-1>{}, j + 1, sb, sa);
+        }
         for (; j + 2 < ntiles; j += 2) {
             step(Flag<true>{}, Flag<false>{}, Phase<-1>{}, j, sa, sb);
             step(Flag<true>{}, Flag<true>{}, Phase<-1>{}, j + 1, sb, sa);

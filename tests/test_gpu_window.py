@@ -35,6 +35,10 @@ CASES = [  # (B, Hq, Hkv, N, d, window, padded)
     (1, 2, 2, 333, 128, (0, 0), False),
     (1, 2, 1, 260, 128, (10000, 10000), True),  # wider than N: plain attention
     (1, 2, 2, 1000, 128, (-1, 0), False),       # unbounded left, right 0: causal
+    # long enough that each wave has masked steps at both window edges and a run of unmasked
+    # steps between them
+    (1, 4, 2, 2000, 128, (700, 300), True),
+    (2, 2, 2, 1500, 64, (257, 33), False),
 ]
 
 
