@@ -316,14 +316,16 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 
 # ------------------------------------------------------------------ main
 
+# The counter recipe written into the summary ($REPO: the repository, $OUT: any writable
+# directory for the counter CSVs).
 TRAFFIC_CMD = """    cd /tmp && export TMPDIR=/tmp
     for C in FETCH_SIZE WRITE_SIZE; do
-      rocprofv3 --pmc $C -T -f csv -d $REPO/gpurun_out/pmc -o bench_$C -- \\
+      rocprofv3 --pmc $C -T -f csv -d $OUT/pmc -o bench_$C -- \\
           python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline --cold-steps 0
-      rocprofv3 --pmc $C -T -f csv -d $REPO/gpurun_out/pmc -o copy_$C -- \\
+      rocprofv3 --pmc $C -T -f csv -d $OUT/pmc -o copy_$C -- \\
           python3 $REPO/bench.py --copy-calib
     done
-    python3 $REPO/bench.py --traffic-summary $REPO/gpurun_out/pmc"""
+    python3 $REPO/bench.py --traffic-summary $OUT/pmc"""
 
 def bench_decode(args):
     """Split-KV decode forward on a decode workload: one step = one fa_fwd_splitkv call (the range
@@ -575,7 +577,7 @@ def main():
         if args.workload != "c3":
             cmd = (cmd.replace("bench.py --steps", f"bench.py --workload {args.workload} --steps")
                       .replace("--traffic-summary", f"--workload {args.workload} --traffic-summary")
-                      .replace("gpurun_out/pmc", "gpurun_out/pmcd"))
+                      .replace("$OUT/pmc", "$OUT/pmcd"))
         traffic_summary(args.traffic_summary, args.workload, cmd)
         return
     if args.gpus != 1:
