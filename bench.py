@@ -303,6 +303,30 @@ def cpu_baseline(x, w, budget_s=20.0):
                       f"host affinity {len(os.sched_getaffinity(0))} cpus"}
 
 
+def sclk_sample(n=5, gap_s=0.004):
+    """The shader clock the driver reports for device 0 (its pp_dpm_sclk file: the line marked
+    '*' is the current level), read n times gap_s apart.  Called while queued steps run."""
+    import re
+
+    import torch
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        path = (f"/sys/bus/pci/devices/{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:"
+                f"{pr.pci_device_id:02x}.0/pp_dpm_sclk")
+        vals = []
+        for _ in range(n):
+            with open(path) as f:
+                for ln in f:
+                    m = re.search(r"(\d+)\s*[Mm][Hh][Zz]", ln) if "*" in ln else None
+                    if m:
+                        vals.append(int(m.group(1)))
+            time.sleep(gap_s)
+        return {"samples": vals, "median": sorted(vals)[len(vals) // 2] if vals else None,
+                "source": path}
+    except Exception as e:   # no such file on this system: report why, measure nothing
+        return {"samples": [], "median": None, "source": f"unavailable ({type(e).__name__})"}
+
+
 def copy_calibration(nbytes=1 << 30, reps=5):
     """A plain device copy of known size for counter calibration (reads and writes nbytes)."""
     import torch
@@ -566,6 +590,9 @@ def main():
                     help="steps timed kernel by kernel after a 512 MiB cache-evicting read "
                          "(reported as kernels_ms_cold_cache; 0 for profiling runs)")
     ap.add_argument("--flush-mib", type=int, default=512, help=argparse.SUPPRESS)
+    ap.add_argument("--sclk-steps", type=int, default=30,
+                    help="steps queued after the timed ones while the shader clock is read "
+                         "(0: no clock reading)")
     ap.add_argument("--splits", type=int, default=0,
                     help="decode workloads: number of key ranges (0: the library's choice)")
     ap.add_argument("--copy-calib", action="store_true")
@@ -657,6 +684,15 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     kern_ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in names}
+    # The shader clock under this load: more steps are queued (outside the timed region) and
+    # the driver's current clock is read while the GPU runs them.
+    sclk = None
+    if args.sclk_steps > 0:
+        for _ in range(args.sclk_steps):
+            step(False)
+        time.sleep(0.005)
+        sclk = sclk_sample()
+        torch.cuda.synchronize()
     # Per-kernel times with cold caches: each launch follows a 512 MiB read that evicts L2 and
     # the Infinity Cache (after the timed steps, with the clocks already up; profiling runs pass
     # --cold-steps 0, so their last dispatches are the timed steps).
@@ -726,6 +762,7 @@ def main():
             "measured_bytes": {n: stored_traffic(n, args.workload)
                                for n in ("bwd_prep", "bwd_dkdv", "bwd_dq")}},
         "roofline": roof,
+        "sclk_mhz_under_load": sclk,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
