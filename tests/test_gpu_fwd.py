@@ -124,6 +124,15 @@ def test_every_output_written_and_canaries_intact():
     assert torch.isnan(lb[:1024]).all() and torch.isnan(lb[1024 + n_l:]).all()
 
 
+def test_bf16_lse_null_gives_the_same_o():
+    """lse = NULL (O only) changes nothing in O, and no LSE is written."""
+    x = gen(2, 4, 2, 333, 128, "bf16", 12, padded=True)
+    o1, l1 = run_fwd(x, True)
+    o2, l2 = run_fwd(x, True, want_lse=False)
+    assert l2 is None and l1 is not None
+    assert torch.equal(o1, o2)
+
+
 def test_forward_is_bitwise_deterministic():
     x = gen(2, 4, 2, 333, 128, "bf16", 10, padded=True)
     o1, l1 = run_fwd(x, True)
