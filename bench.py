@@ -741,6 +741,8 @@ def main():
                    "seed": w.seed, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {n: round(t, 4) for n, t in kern_ms.items()},
+        "kernels_ms_median": {n: round(sorted(a.elapsed_time(b) for a, b in ev[n])[len(ev[n]) // 2], 4)
+                              for n in names},
         "kernels_ms_cold_cache": None if args.cold_steps <= 0 else {
             n: round(sum(a.elapsed_time(b) for a, b in cold[n]) / len(cold[n]), 4) for n in names},
         "fwd": None if not do_fwd else {
