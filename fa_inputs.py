@@ -123,6 +123,30 @@ def make(w: Workload, want_do: bool | None = None) -> dict:
     return out
 
 
+def make_on_device(w: Workload, device) -> dict:
+    """The same recipe drawn by a seeded generator on ``device``, for workloads too large to
+    draw on the host (tensors of more than 2^31 elements).  The values differ from ``make``'s for
+    the same seed (another generator), but are drawn the same way: Q, K, V iid N(0, 1) times the
+    workload's standard deviation, rounded to its dtype, then the key lengths (padded workloads)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    dt = _TORCH_DTYPE[w.dtype]
+
+    def draw(*shape):
+        t = torch.empty(*shape, dtype=dt, device=device)
+        for i in range(shape[0]):   # one batch at a time: the fp32 draw is 2x the bf16 tensor
+            t[i] = (torch.randn(*shape[1:], generator=g, dtype=torch.float32, device=device)
+                    * w.std).to(dt)
+        return t
+
+    out = {"q": draw(w.B, w.Hq, w.N, w.d), "k": draw(w.B, w.Hkv, w.N, w.d),
+           "v": draw(w.B, w.Hkv, w.N, w.d), "do": None, "key_lens": None, "scale": w.scale}
+    if w.padded:
+        out["key_lens"] = torch.randint(w.N // 2, w.N + 1, (w.B,), generator=g, dtype=torch.int32,
+                                        device=device)
+    return out
+
+
 @dataclass(frozen=True)
 class DecodeWorkload:
     """Decode shape: Nq query rows per q-head against Nk cached keys per kv-head."""

@@ -194,6 +194,33 @@ def test_full_size_workload_sampled_rows(name):
     check_close("LSE", np64(lse[idx]), LSE, TOL_LSE)
 
 
+def test_tensors_past_2_31_elements():
+    """Q and O of more than 2^31 elements (4.8 GB each): the kernel's addressing is 64-bit.  Rows
+    of the first and of the last batch and head (element offsets past 2^31) are recomputed by the
+    oracle one by one; every output is checked for finiteness.  Grouped heads and key lengths as
+    in the largest workload."""
+    w = fi.Workload("big", 9, 64, 8, 32768, 128, "bf16", True, True, False, 1.0, 11)
+    assert w.B * w.Hq * w.N * w.d > 2**31
+    print(f"\n> 2^31 elements: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d}", flush=True)
+    x = fi.make_on_device(w, DEV)
+    o, lse = fa.fa_fwd(x["q"], x["k"], x["v"], scale=x["scale"], causal=True,
+                       key_lens=x["key_lens"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    picks = sorted({(b, h, i) for b in (0, w.B - 1) for h in (0, w.Hq - 1)
+                    for i in (0, 1, 127, 128, w.N // 2, w.N - 2, w.N - 1)}
+                   | {(w.B - 1, int(h), int(i)) for h, i in
+                      zip(np.random.default_rng(11).integers(w.Hq, size=8),
+                          np.random.default_rng(12).integers(w.N, size=8))})
+    kl = x["key_lens"].cpu()
+    O, LSE = attn_fwd_rows(x["q"], x["k"], x["v"], x["scale"], True, kl, picks)
+    idx = tuple(torch.tensor(a) for a in zip(*picks))
+    check_close("O", np64(o[idx]), O, TOL_BF16_MAX, TOL_BF16_MEAN)
+    check_close("LSE", np64(lse[idx]), LSE, TOL_LSE)
+    del x, o, lse
+    torch.cuda.empty_cache()
+
+
 def test_c2_two_heads_in_full():
     w = fi.WORKLOADS["c2"]
     x = fi.make(w)
