@@ -11,5 +11,5 @@ this package.  The HIP library and its Python binding never do; the two share no
 Every function here is pinned by the ``-m "not gpu"`` tests against values the pages print,
 closed forms, invariants, an independent library routine and brute force.
 """
-from .naive import (attn_bwd, attn_bwd_heads, attn_decode, attn_fwd, attn_fwd_rows,  # noqa: F401
-                    kv_head_of, score_rows, to64, visible_mask)
+from .naive import (attn_bwd, attn_bwd_heads, attn_decode, attn_dq_rows, attn_fwd,  # noqa: F401
+                    attn_fwd_rows, kv_head_of, score_rows, to64, visible_mask)

@@ -46,7 +46,7 @@ import numpy as np
 
 __all__ = [
     "to64", "kv_head_of", "visible_mask", "attn_fwd", "attn_fwd_rows",
-    "attn_bwd", "attn_bwd_heads", "score_rows", "attn_decode",
+    "attn_bwd", "attn_bwd_heads", "attn_dq_rows", "score_rows", "attn_decode",
 ]
 
 
@@ -217,6 +217,35 @@ def attn_fwd_rows(q, k, v, scale: float, causal: bool, key_lens, picks, window=N
         O[n] = (P @ V)[0]
         LSE[n] = m[0] + np.log(l[0]) if np.isfinite(m[0]) else -np.inf
     return O, LSE
+
+
+def attn_dq_rows(q, k, v, do, scale: float, causal: bool, key_lens, picks):
+    """dQ of individual query rows: ``picks`` is a list of (b, h, i); returns [len(picks), d].
+
+    dQ_i needs only row i of P and of dP (the softmax derivative is row-wise): with
+    P_i = softmax(scale q_i K^T) over the visible keys, dP_i = dO_i V^T and D_i = sum_j P_ij dP_ij,
+    dQ_i = scale * sum_j P_ij (dP_ij - D_i) K_j.  Each row costs O(N d), so full-size workloads
+    can be checked on sampled rows.  A row with no visible key gets dQ_i = 0.
+    """
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    lens = _lens(key_lens, B, N)
+    out = np.zeros((len(picks), d))
+    cache = {}
+    for n, (b, h, i) in enumerate(picks):
+        g = kv_head_of(h, Hq, Hkv)
+        L = lens[b]
+        if (b, g) not in cache:
+            cache[(b, g)] = (to64(k[b, g, :L]), to64(v[b, g, :L]))
+        K, V = cache[(b, g)]
+        s = score_rows(to64(q[b, h, i:i + 1]), K, scale)
+        P, m, _ = _softmax_rows(s, visible_mask(np.array([i]), L, causal))
+        if not np.isfinite(m[0]):
+            continue
+        dP = to64(do[b, h, i:i + 1]) @ V.T
+        Di = (P * dP).sum()
+        out[n] = float(scale) * ((P * (dP - Di)) @ K)[0]
+    return out
 
 
 def attn_bwd(q, k, v, do, scale: float, causal: bool = False, key_lens=None,

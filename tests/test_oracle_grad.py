@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attn_bwd, attn_bwd_heads, attn_fwd
+from oracle import attn_bwd, attn_bwd_heads, attn_dq_rows, attn_fwd
 from oracle.fd import numeric_grads
 
 
@@ -85,3 +85,41 @@ def test_heads_api_matches_full():
         np.testing.assert_allclose(gq, dQ[b, 2 * g:2 * g + 2], atol=1e-15)
         np.testing.assert_allclose(gk, dK[b, g], atol=1e-15)
         np.testing.assert_allclose(gv, dV[b, g], atol=1e-15)
+
+
+@pytest.mark.parametrize("causal,lens,Hq,Hkv", [
+    (False, None, 2, 2), (True, None, 4, 2), (True, [19, 33], 4, 1)])
+def test_dq_rows_match_torch_autograd_float64(causal, lens, Hq, Hkv):
+    """The per-row dQ against torch float64 autograd through its SDPA math path."""
+    q, k, v, do = _rand(13, 2, Hq, Hkv, 40, 16)
+    tq = torch.from_numpy(q).requires_grad_()
+    G = Hq // Hkv
+    mask = torch.ones(2, 1, 40, 40, dtype=torch.bool)
+    if causal:
+        mask &= torch.ones(40, 40, dtype=torch.bool).tril()
+    if lens is not None:
+        mask &= (torch.arange(40)[None, :] < torch.tensor(lens)[:, None])[:, None, None, :]
+    O = torch.nn.functional.scaled_dot_product_attention(
+        tq, torch.from_numpy(k).repeat_interleave(G, 1), torch.from_numpy(v).repeat_interleave(G, 1),
+        attn_mask=mask, scale=0.25)
+    O.backward(torch.from_numpy(do))
+    picks = [(b, h, i) for b in range(2) for h in range(Hq) for i in (0, 1, 18, 19, 32, 39)]
+    got = attn_dq_rows(q, k, v, do, 0.25, causal, lens, picks)
+    ref = np.stack([tq.grad.numpy()[b, h, i] for b, h, i in picks])
+    np.testing.assert_allclose(got, ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,lens", [(False, None), (True, [5, 3])])
+def test_dq_rows_match_finite_differences(causal, lens):
+    q, k, v, do = _rand(14, 2, 4, 2, 6, 3)
+    nQ, _, _ = numeric_grads(q, k, v, do, 0.8, causal, lens)
+    picks = [(b, h, i) for b in range(2) for h in range(4) for i in range(6)]
+    got = attn_dq_rows(q, k, v, do, 0.8, causal, lens, picks)
+    np.testing.assert_allclose(got, np.stack([nQ[b, h, i] for b, h, i in picks]),
+                               rtol=1e-6, atol=1e-8)
+
+
+def test_dq_rows_of_a_batch_with_no_keys_are_zero():
+    q, k, v, do = _rand(15, 2, 2, 2, 8, 4)
+    got = attn_dq_rows(q, k, v, do, 0.5, True, [0, 8], [(0, 1, 3), (1, 0, 5)])
+    assert np.all(got[0] == 0) and np.any(got[1] != 0)
