@@ -141,6 +141,8 @@ def make_on_device(w: Workload, device) -> dict:
 
     out = {"q": draw(w.B, w.Hq, w.N, w.d), "k": draw(w.B, w.Hkv, w.N, w.d),
            "v": draw(w.B, w.Hkv, w.N, w.d), "do": None, "key_lens": None, "scale": w.scale}
+    if w.backward:
+        out["do"] = draw(w.B, w.Hq, w.N, w.d)
     if w.padded:
         out["key_lens"] = torch.randint(w.N // 2, w.N + 1, (w.B,), generator=g, dtype=torch.int32,
                                         device=device)

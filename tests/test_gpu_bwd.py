@@ -5,7 +5,7 @@ import torch
 
 import exact_io_aware_68_amd as fa
 import fa_inputs as fi
-from oracle import attn_bwd, attn_bwd_heads, attn_fwd
+from oracle import attn_bwd, attn_bwd_heads, attn_dq_rows, attn_fwd
 from tests._parity import TOL_BF16_MAX, TOL_BF16_MEAN, check_close, np64
 
 pytestmark = pytest.mark.gpu
@@ -162,3 +162,33 @@ def test_c5_full_size_sampled_heads():
     sdv = dv.double().sum(2).cpu()
     sdo = x["do"].double().sum(2)
     assert (sdv - sdo).abs().max().item() < 0.5
+
+
+def test_backward_tensors_past_2_31_elements():
+    """Backward on Q, O, dO and an fp32 dQ of more than 2^31 elements (dQ 9.7 GB): the kernels'
+    addressing is 64-bit.  dQ rows of the first and of the last batch and head (offsets past
+    2^31) against the oracle's per-row dQ; every gradient finite; for every kv-head,
+    sum_j dV_j equals the sum of dO over its query heads' rows (rows of P sum to one)."""
+    w = fi.Workload("bigb", 9, 64, 8, 32768, 128, "bf16", True, True, True, 1.0, 13)
+    assert w.B * w.Hq * w.N * w.d > 2**31
+    print(f"\n> 2^31 elements, backward: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d}", flush=True)
+    x = fi.make_on_device(w, DEV)
+    kl = x["key_lens"]
+    o, lse = fa.fa_fwd(x["q"], x["k"], x["v"], scale=x["scale"], causal=True, key_lens=kl)
+    dq, dk, dv = fa.fa_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, scale=x["scale"], causal=True,
+                           key_lens=kl)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+    del o, lse
+    picks = sorted({(b, h, i) for b in (0, w.B - 1) for h in (0, w.Hq - 1)
+                    for i in (0, 1, 127, 128, w.N // 2, w.N - 2, w.N - 1)})
+    ref = attn_dq_rows(x["q"], x["k"], x["v"], x["do"], x["scale"], True, kl.cpu(), picks)
+    idx = tuple(torch.tensor(a) for a in zip(*picks))
+    check_close("dQ", np64(dq[idx]), ref, TOL_BF16_MAX, TOL_BF16_MEAN)
+    G = w.Hq // w.Hkv
+    sdv = dv.double().sum(2)                                            # [B, Hkv, d]
+    sdo = x["do"].double().sum(2).view(w.B, w.Hkv, G, w.d).sum(2)       # [B, Hkv, d]
+    assert (sdv - sdo).abs().max().item() < 1.0
+    del x, dq, dk, dv
+    torch.cuda.empty_cache()
