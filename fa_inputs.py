@@ -192,6 +192,27 @@ def make_decode(w: DecodeWorkload) -> dict:
     return out
 
 
+def make_decode_on_device(w: DecodeWorkload, device) -> dict:
+    """``make_decode``'s recipe drawn by a seeded generator on ``device`` (for caches of more than
+    2^31 elements); the values differ from ``make_decode``'s for the same seed."""
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+
+    def draw(*shape):
+        t = torch.empty(*shape, dtype=torch.bfloat16, device=device)
+        for i in range(shape[0]):
+            t[i] = (torch.randn(*shape[1:], generator=g, dtype=torch.float32, device=device)
+                    * w.std).to(torch.bfloat16)
+        return t
+
+    out = {"q": draw(w.B, w.Hq, w.Nq, w.d), "k": draw(w.B, w.Hkv, w.Nk, w.d),
+           "v": draw(w.B, w.Hkv, w.Nk, w.d), "key_lens": None, "scale": w.scale}
+    if w.padded:
+        out["key_lens"] = torch.randint(w.Nk // 2, w.Nk + 1, (w.B,), generator=g,
+                                        dtype=torch.int32, device=device)
+    return out
+
+
 def worked_example() -> dict:
     """The tutorial page's worked example (N = 4, d = 2): Q = K, V as printed, scale 1/sqrt(2)."""
     q = torch.tensor([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0], [0.0, 0.0]])

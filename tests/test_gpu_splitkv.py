@@ -100,3 +100,25 @@ def test_decode_workload_full():
     O, LSE = attn_decode(x["q"], x["k"], x["v"], x["scale"], x["key_lens"])
     check_close("O", np64(o), O, TOL_BF16_MAX, TOL_BF16_MEAN)
     check_close("LSE", np64(lse), LSE, TOL_LSE)
+
+
+def test_cache_past_2_31_elements():
+    """K and V caches of more than 2^31 elements each (72 sequences of 32768 keys, 4.8 GB each):
+    the range kernel's and the merge's addressing is 64-bit.  The first and the last sequence
+    (cache offsets past 2^31) are checked in full against the oracle; every row is finite."""
+    w = fi.DecodeWorkload("bigd", 72, 32, 8, 1, 32768, 128, True, 1.0, 17)
+    assert w.B * w.Hkv * w.Nk * w.d > 2**31
+    print(f"\n> 2^31-element cache: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} d={w.d}",
+          flush=True)
+    x = fi.make_decode_on_device(w, DEV)
+    kl = x["key_lens"]
+    o, lse = fa.fa_fwd_splitkv(x["q"], x["k"], x["v"], scale=x["scale"], key_lens=kl)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    for b in (0, w.B - 1):
+        sl = slice(b, b + 1)
+        O, LSE = attn_decode(x["q"][sl], x["k"][sl], x["v"][sl], x["scale"], kl[sl].cpu())
+        check_close("O", np64(o[sl]), O, TOL_BF16_MAX, TOL_BF16_MEAN)
+        check_close("LSE", np64(lse[sl]), LSE, TOL_LSE)
+    del x, o, lse
+    torch.cuda.empty_cache()
