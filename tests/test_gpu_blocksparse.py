@@ -110,3 +110,29 @@ def test_sparse_workload_sampled_rows():
     idx = tuple(torch.tensor(a) for a in zip(*picks))
     check_close("O", np64(o[idx]), O, TOL_BF16_MAX, TOL_BF16_MEAN)
     check_close("LSE", np64(lse[idx]), LSE, TOL_LSE)
+
+
+def test_sparse_past_2_31_elements():
+    """Q and O of more than 2^31 elements under a block bitmap (causal, grouped heads, key
+    lengths): the sparse kernel's addressing is 64-bit.  Rows of the first and of the last batch
+    and head against the oracle; every output finite."""
+    w = fi.Workload("bigs", 9, 64, 8, 32768, 128, "bf16", True, True, False, 1.0, 19)
+    assert w.B * w.Hq * w.N * w.d > 2**31
+    print(f"\n> 2^31 elements, block-sparse: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d}",
+          flush=True)
+    x = fi.make_on_device(w, DEV)
+    bm = fi.block_bitmap(w.N, 0.1, 19)
+    kl = x["key_lens"]
+    o, lse = fa.fa_fwd_blocksparse(x["q"], x["k"], x["v"], bm.to(DEV), scale=x["scale"],
+                                   causal=True, key_lens=kl)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    picks = sorted({(b, h, i) for b in (0, w.B - 1) for h in (0, w.Hq - 1)
+                    for i in (0, 1, 127, 128, w.N // 2, w.N - 2, w.N - 1)})
+    O, LSE = attn_fwd_rows(x["q"], x["k"], x["v"], x["scale"], True, kl.cpu(), picks,
+                           block_mask=(bm.numpy(), fa.BLOCK_Q, fa.BLOCK_K))
+    idx = tuple(torch.tensor(a) for a in zip(*picks))
+    check_close("O", np64(o[idx]), O, TOL_BF16_MAX, TOL_BF16_MEAN)
+    check_close("LSE", np64(lse[idx]), LSE, TOL_LSE)
+    del x, o, lse
+    torch.cuda.empty_cache()
