@@ -98,3 +98,22 @@ def test_splitkv_outputs_and_workspace():
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
     assert guards_intact(ob) and guards_intact(lb)
     assert (wsb[:G] == 0xFF).all() and (wsb[-G:] == 0xFF).all()
+
+
+def test_variants_are_bitwise_deterministic():
+    """No atomics anywhere: repeated calls give identical bits (window, block-sparse, split-KV
+    with several ranges)."""
+    x = inputs(2, 4, 2, 333, 128, 25, [333, 201])
+    bm = fi.block_bitmap(333, 0.3, 25).to(DEV)
+    runs = []
+    for _ in range(2):
+        a = fa.fa_fwd_window(x["q"], x["k"], x["v"], window=(40, 40), scale=x["scale"],
+                             key_lens=x["key_lens"])
+        b = fa.fa_fwd_blocksparse(x["q"], x["k"], x["v"], bm, scale=x["scale"], causal=True,
+                                  key_lens=x["key_lens"])
+        c = fa.fa_fwd_splitkv(x["q"][:, :, :3].contiguous(), x["k"], x["v"], scale=x["scale"],
+                              key_lens=x["key_lens"], num_splits=3)
+        torch.cuda.synchronize()
+        runs.append([t.clone() for t in (*a, *b, *c)])
+    for t1, t2 in zip(*runs):
+        assert torch.equal(t1, t2)
