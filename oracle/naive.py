@@ -95,6 +95,13 @@ def visible_mask(rows: np.ndarray, L: int, causal: bool, window=None,
     return vis
 
 
+def _softmax_vjp(P: np.ndarray, dP: np.ndarray) -> np.ndarray:
+    """Softmax derivative contracted row by row: dS = P * (dP - D) with D_i = sum_j P_ij dP_ij
+    (rows of P over the visible keys; invisible entries have P = 0 and get dS = 0)."""
+    D = (P * dP).sum(axis=1)
+    return P * (dP - D[:, None])
+
+
 def _lens(key_lens, B: int, N: int) -> list[int]:
     if key_lens is None:
         return [N] * B
@@ -243,8 +250,7 @@ def attn_dq_rows(q, k, v, do, scale: float, causal: bool, key_lens, picks):
         if not np.isfinite(m[0]):
             continue
         dP = to64(do[b, h, i:i + 1]) @ V.T
-        Di = (P * dP).sum()
-        out[n] = float(scale) * ((P * (dP - Di)) @ K)[0]
+        out[n] = float(scale) * (_softmax_vjp(P, dP) @ K)[0]
     return out
 
 
@@ -277,8 +283,7 @@ def attn_bwd(q, k, v, do, scale: float, causal: bool = False, key_lens=None,
                 P, _, _ = _softmax_rows(s, visible_mask(rows, L, causal))
                 dO = do[b, h, rows]
                 dP = dO @ V.T
-                D = (P * dP).sum(axis=1)
-                dS = P * (dP - D[:, None])
+                dS = _softmax_vjp(P, dP)
                 dQ[b, h, rows] = scale * (dS @ K)
                 dK[b, g, :L] += scale * (dS.T @ q[b, h, rows])
                 dV[b, g, :L] += P.T @ dO
