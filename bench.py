@@ -641,7 +641,7 @@ def main():
     dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
     dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
     dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
-    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.Hq, w.N, w.d), dtype=torch.uint8, device=dev)
+    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.Hq, w.N), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     do_fwd = args.only in ("fwd", "both")
     do_bwd = args.only in ("bwd", "both")

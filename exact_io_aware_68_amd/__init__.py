@@ -73,7 +73,7 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_dkdv.restype = I
     lib.fa_bwd_dq.argtypes = [P, P, P, P, P, P, P, Z, I, I, I, I, I, F, I, I, P]
     lib.fa_bwd_dq.restype = I
-    lib.fa_bwd_workspace_size.argtypes = [I, I, I, I]
+    lib.fa_bwd_workspace_size.argtypes = [I, I, I]
     lib.fa_bwd_workspace_size.restype = Z
     lib.fa_fwd_blocksparse.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.fa_fwd_blocksparse.restype = I
@@ -104,8 +104,8 @@ def fa_abi_version() -> int:
     return load().fa_abi_version()
 
 
-def fa_bwd_workspace_size(B: int, Hq: int, N: int, d: int) -> int:
-    return int(load().fa_bwd_workspace_size(B, Hq, N, d))
+def fa_bwd_workspace_size(B: int, Hq: int, N: int) -> int:
+    return int(load().fa_bwd_workspace_size(B, Hq, N))
 
 
 def fa_fwd_kernel_name(d: int, causal: bool, has_key_lens: bool, dtype: int) -> str:
@@ -147,13 +147,49 @@ def _stream(stream, device) -> int:
     return stream.cuda_stream
 
 
-def _shape(q, k):
-    if q.dim() != 4 or k.dim() != 4:
-        raise ValueError("q, k, v must be 4-D [B, H, N, d]")
+# Every tensor is checked before the library is called: the C ABI sees raw pointers only, so a
+# wrong shape, dtype, stride or device would otherwise be read or written out of bounds on the
+# GPU.  Device checks come last, so that the shape rules can be exercised on the CPU.
+
+def _need(cond: bool, fn: str, msg: str):
+    if not cond:
+        raise ValueError(f"{fn}: {msg}")
+
+
+def _tensor(fn: str, name: str, t, shape=None, dtype=None):
+    """t must be a contiguous tensor, with the given shape and dtype when those are given."""
+    _need(hasattr(t, "is_contiguous"), fn, f"{name} must be a torch tensor")
+    _need(t.is_contiguous(), fn, f"{name} must be contiguous")
+    if shape is not None:
+        _need(tuple(t.shape) == tuple(shape), fn,
+              f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None:
+        _need(t.dtype == dtype, fn, f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _qkv(fn: str, q, k, v, key_lens):
+    """q [B, Hq, N, d], k and v [B, Hkv, N, d] of q's dtype (bf16 or fp32), key_lens int32 [B]."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _tensor(fn, name, t)
+        _need(t.dim() == 4, fn, f"{name} must be 4-D [B, H, N, d]")
+    _need(q.dtype in (torch.bfloat16, torch.float32), fn, "q must be bfloat16 or float32")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, fn, "q, k and v must share one dtype")
+    _need(tuple(v.shape) == tuple(k.shape), fn, "k and v must have the same shape")
     B, Hq, N, d = q.shape
-    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
-        raise ValueError("k/v shape does not match q")
+    _need(k.shape[0] == B and k.shape[2] == N and k.shape[3] == d, fn,
+          "k/v shape does not match q ([B, Hkv, N, d])")
+    if key_lens is not None:
+        _tensor(fn, "key_lens", key_lens, (B,), torch.int32)
     return B, Hq, k.shape[1], N, d
+
+
+def _on_one_gpu(fn: str, *tensors):
+    """Every tensor given (None skipped) lives on one and the same GPU."""
+    ts = [t for t in tensors if t is not None]
+    for t in ts:
+        _need(t.is_cuda, fn, f"every tensor must be on a GPU (found one on {t.device})")
+    _need(len({t.device for t in ts}) <= 1, fn, "all tensors must be on the same GPU")
 
 
 def _check(fn: str, status: int):
@@ -165,20 +201,27 @@ def _default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
 
+def _fwd_outputs(fn: str, q, o, lse, rows=None):
+    """Caller-supplied o must match q; lse must be fp32 [B, Hq, N] (rows = N, or Nq)."""
+    torch = _torch()
+    B, Hq, N = q.shape[0], q.shape[1], q.shape[2] if rows is None else rows
+    if o is not None:
+        _tensor(fn, "o", o, q.shape, q.dtype)
+    if lse is not None:
+        _tensor(fn, "lse", lse, (B, Hq, N), torch.float32)
+
+
 def fa_fwd(q, k, v, *, scale: float | None = None, causal: bool = False, key_lens=None,
            o=None, lse=None, want_lse: bool = True, stream=None):
     """Forward attention through libfa.so.  Returns (o, lse); lse is None if not wanted."""
     torch = _torch()
-    B, Hq, Hkv, N, d = _shape(q, k)
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("inputs must be contiguous")
+    B, Hq, Hkv, N, d = _qkv("fa_fwd", q, k, v, key_lens)
+    _fwd_outputs("fa_fwd", q, o, lse)
+    _on_one_gpu("fa_fwd", q, k, v, key_lens, o, lse)
     if o is None:
         o = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    if key_lens is not None and key_lens.dtype != torch.int32:
-        raise ValueError("key_lens must be int32")
     st = load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(key_lens), B, Hq,
                        Hkv, N, d, ctypes.c_float(_default_scale(d) if scale is None else scale),
                        int(causal), _dtype_code(q), _stream(stream, q.device))
@@ -191,16 +234,13 @@ def fa_fwd_window(q, k, v, *, window, scale: float | None = None, key_lens=None,
     """Forward with a local window (left, right): row i sees keys i - left .. i + right (a
     negative side is unbounded).  Returns (o, lse)."""
     torch = _torch()
-    B, Hq, Hkv, N, d = _shape(q, k)
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("inputs must be contiguous")
+    B, Hq, Hkv, N, d = _qkv("fa_fwd_window", q, k, v, key_lens)
+    _fwd_outputs("fa_fwd_window", q, o, lse)
+    _on_one_gpu("fa_fwd_window", q, k, v, key_lens, o, lse)
     if o is None:
         o = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    if key_lens is not None and key_lens.dtype != torch.int32:
-        raise ValueError("key_lens must be int32")
     left, right = window
     st = load().fa_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(key_lens), B,
                               Hq, Hkv, N, d,
@@ -215,19 +255,15 @@ def fa_fwd_blocksparse(q, k, v, block_mask, *, scale: float | None = None, causa
     """Block-sparse forward: block_mask is a uint8 device tensor [ceil(N/128), ceil(N/64)];
     row i sees key j only where block_mask[i // 128, j // 64] != 0.  Returns (o, lse)."""
     torch = _torch()
-    B, Hq, Hkv, N, d = _shape(q, k)
-    for t in (q, k, v, block_mask):
-        if not t.is_contiguous():
-            raise ValueError("inputs must be contiguous")
-    if block_mask.dtype != torch.uint8 or tuple(block_mask.shape) != (
-            -(-N // BLOCK_Q), -(-N // BLOCK_K)):
-        raise ValueError("block_mask must be uint8 [ceil(N/128), ceil(N/64)]")
+    fn = "fa_fwd_blocksparse"
+    B, Hq, Hkv, N, d = _qkv(fn, q, k, v, key_lens)
+    _tensor(fn, "block_mask", block_mask, (-(-N // BLOCK_Q), -(-N // BLOCK_K)), torch.uint8)
+    _fwd_outputs(fn, q, o, lse)
+    _on_one_gpu(fn, q, k, v, key_lens, block_mask, o, lse)
     if o is None:
         o = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    if key_lens is not None and key_lens.dtype != torch.int32:
-        raise ValueError("key_lens must be int32")
     st = load().fa_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(key_lens),
                                    _ptr(block_mask), B, Hq, Hkv, N, d,
                                    ctypes.c_float(_default_scale(d) if scale is None else scale),
@@ -236,7 +272,36 @@ def fa_fwd_blocksparse(q, k, v, block_mask, *, scale: float | None = None, causa
     return o, lse
 
 
+def _workspace(fn: str, ws):
+    _tensor(fn, "workspace", ws)
+
+
+def _grad_inputs(fn: str, q, dO, o=None, lse=None):
+    """dO (and o) like q; lse fp32 [B, Hq, N]."""
+    torch = _torch()
+    _tensor(fn, "dO", dO, q.shape, q.dtype)
+    if o is not None:
+        _tensor(fn, "o", o, q.shape, q.dtype)
+    if lse is not None:
+        _tensor(fn, "lse", lse, q.shape[:3], torch.float32)
+
+
+def _grad_outputs(fn: str, q, k, dq=None, dk=None, dv=None):
+    """fp32 gradients: dq like q, dk and dv like k."""
+    torch = _torch()
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
+        if t is not None:
+            _tensor(fn, name, t, like.shape, torch.float32)
+
+
 def fa_bwd_prep(o, dO, lse, workspace, *, stream=None):
+    torch = _torch()
+    fn = "fa_bwd_prep"
+    _tensor(fn, "o", o)
+    _need(o.dim() == 4 and o.dtype == torch.bfloat16, fn, "o must be bf16 [B, Hq, N, d]")
+    _grad_inputs(fn, o, dO, None, lse)
+    _workspace(fn, workspace)
+    _on_one_gpu(fn, o, dO, lse, workspace)
     B, Hq, N, d = o.shape
     st = load().fa_bwd_prep(_ptr(o), _ptr(dO), _ptr(lse), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), B, Hq, N, d,
@@ -246,7 +311,13 @@ def fa_bwd_prep(o, dO, lse, workspace, *, stream=None):
 
 def fa_bwd_dkdv(q, k, v, dO, dk, dv, workspace, *, scale=None, causal=False, key_lens=None,
                 stream=None):
-    B, Hq, Hkv, N, d = _shape(q, k)
+    fn = "fa_bwd_dkdv"
+    B, Hq, Hkv, N, d = _qkv(fn, q, k, v, key_lens)
+    _grad_inputs(fn, q, dO)
+    _need(dk is not None and dv is not None, fn, "dk and dv are required")
+    _grad_outputs(fn, q, k, None, dk, dv)
+    _workspace(fn, workspace)
+    _on_one_gpu(fn, q, k, v, dO, key_lens, dk, dv, workspace)
     st = load().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(key_lens), _ptr(dk),
                             _ptr(dv), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), B, Hq, Hkv, N, d,
@@ -257,7 +328,13 @@ def fa_bwd_dkdv(q, k, v, dO, dk, dv, workspace, *, scale=None, causal=False, key
 
 def fa_bwd_dq(q, k, v, dO, dq, workspace, *, scale=None, causal=False, key_lens=None,
               stream=None):
-    B, Hq, Hkv, N, d = _shape(q, k)
+    fn = "fa_bwd_dq"
+    B, Hq, Hkv, N, d = _qkv(fn, q, k, v, key_lens)
+    _grad_inputs(fn, q, dO)
+    _need(dq is not None, fn, "dq is required")
+    _grad_outputs(fn, q, k, dq)
+    _workspace(fn, workspace)
+    _on_one_gpu(fn, q, k, v, dO, key_lens, dq, workspace)
     st = load().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(key_lens), _ptr(dq),
                           _ptr(workspace), workspace.numel() * workspace.element_size(), B, Hq,
                           Hkv, N, d, ctypes.c_float(_default_scale(d) if scale is None else scale),
@@ -269,13 +346,19 @@ def fa_bwd(q, k, v, o, dO, lse, *, scale: float | None = None, causal: bool = Fa
            key_lens=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
     """Backward by recomputation through libfa.so.  Returns (dq, dk, dv) in fp32."""
     torch = _torch()
-    B, Hq, Hkv, N, d = _shape(q, k)
+    fn = "fa_bwd"
+    B, Hq, Hkv, N, d = _qkv(fn, q, k, v, key_lens)
+    _grad_inputs(fn, q, dO, o, lse)
+    _grad_outputs(fn, q, k, dq, dk, dv)
+    if workspace is not None:
+        _workspace(fn, workspace)
+    _on_one_gpu(fn, q, k, v, o, dO, lse, key_lens, dq, dk, dv, workspace)
     f32 = dict(dtype=torch.float32, device=q.device)
     dq = torch.empty(q.shape, **f32) if dq is None else dq
     dk = torch.empty(k.shape, **f32) if dk is None else dk
     dv = torch.empty(v.shape, **f32) if dv is None else dv
     if workspace is None:
-        workspace = torch.empty(max(1, fa_bwd_workspace_size(B, Hq, N, d)), dtype=torch.uint8,
+        workspace = torch.empty(max(1, fa_bwd_workspace_size(B, Hq, N)), dtype=torch.uint8,
                                 device=q.device)
     st = load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(key_lens),
                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
@@ -300,17 +383,22 @@ def fa_fwd_splitkv(q, k, v, *, scale: float | None = None, key_lens=None, num_sp
     """Split-KV forward for decode shapes: q [B, Hq, Nq, d] against k, v [B, Hkv, Nk, d]; every
     query row sees keys [0, key_lens[b]).  Returns (o, lse); lse is None if not wanted."""
     torch = _torch()
-    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
-        raise ValueError("q, k, v must be 4-D [B, H, N, d] with k and v of one shape")
+    fn = "fa_fwd_splitkv"
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _tensor(fn, name, t)
+        _need(t.dim() == 4, fn, f"{name} must be 4-D [B, H, N, d]")
+    _need(q.dtype in (torch.bfloat16, torch.float32), fn, "q must be bfloat16 or float32")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, fn, "q, k and v must share one dtype")
+    _need(tuple(v.shape) == tuple(k.shape), fn, "k and v must have the same shape")
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
-    if k.shape[0] != B or k.shape[3] != d:
-        raise ValueError("k/v shape does not match q")
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("inputs must be contiguous")
-    if key_lens is not None and key_lens.dtype != torch.int32:
-        raise ValueError("key_lens must be int32")
+    _need(k.shape[0] == B and k.shape[3] == d, fn, "k/v shape does not match q ([B, Hkv, Nk, d])")
+    if key_lens is not None:
+        _tensor(fn, "key_lens", key_lens, (B,), torch.int32)
+    _fwd_outputs(fn, q, o, lse, rows=Nq)
+    if workspace is not None:
+        _workspace(fn, workspace)
+    _on_one_gpu(fn, q, k, v, key_lens, o, lse, workspace)
     if o is None:
         o = torch.empty_like(q)
     if lse is None and want_lse:

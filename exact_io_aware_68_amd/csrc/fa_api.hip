@@ -10,15 +10,35 @@ namespace {
 
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
-// Shapes: sizes non-negative, head counts positive, element counts within int64 and the grid.
+// Shapes: sizes non-negative, head counts positive, element counts within int64.
 fa_status check_shape(int B, int Hq, int Hkv, int N, int d) {
     if (B < 0 || N < 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return FA_ERR_SHAPE;
     const long double elems = (long double)B * Hq * N * d;
     if (elems > 9.0e18L) return FA_ERR_SHAPE;
-    // 1-D grids: tiles x heads must fit an unsigned grid dimension.
-    if ((long double)B * Hq * ((N + 63) / 64) > 4.0e9L) return FA_ERR_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_GQA;
     return FA_OK;
+}
+
+// Every launch here is a 1-D grid, and HIP limits a grid dimension to fewer than 2^32
+// work-items: `blocks` workgroups of `threads` work-items must stay below that (the kernels also
+// index workgroups with 32-bit ints, which this bound keeps far from overflow).  Computed in
+// long double so that no product of the int arguments can wrap.
+bool grid_fits(long double blocks, int threads) {
+    return blocks * (long double)threads < 4294967296.0L;
+}
+long double tiles(int n, int t) { return (long double)((n + (long long)t - 1) / t); }
+
+// Workgroup counts of the launches (kernel files: fa_fwd_bf16.hip, fa_fwd_f32.hip,
+// fa_fwd_sparse.hip, fa_bwd_bf16.hip, fa_bwd_dq.hip, fa_splitkv.hip).
+bool fwd_grid_fits(int B, int Hq, int N, fa_dtype dtype) {
+    if (dtype == FA_F32) return grid_fits((long double)B * Hq * tiles(N, 64), 64);
+    return grid_fits((long double)B * Hq * tiles(N, 128), 256);
+}
+bool bwd_grid_fits(int B, int Hq, int Hkv, int N, int d) {
+    const int rows_per_block = 256 / (d / 8);   // prep: d/8 lanes per row
+    return grid_fits(ceill((long double)B * Hq * N / rows_per_block), 256) &&
+           grid_fits((long double)B * Hkv * tiles(N, 128), 512) &&   // dK, dV
+           grid_fits((long double)B * Hq * tiles(N, 128), 256);      // dQ
 }
 
 fa_status check_scale(float scale) {
@@ -96,6 +116,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     if (dtype == FA_BF16 && d != 64 && d != 128) return FA_ERR_HEADDIM;
     if (dtype == FA_F32 && d > 128) return FA_ERR_HEADDIM;
     if ((st = check_scale(scale)) != FA_OK) return st;
+    if (!fwd_grid_fits(B, Hq, N, dtype)) return FA_ERR_SHAPE;
     if (B == 0 || N == 0) return FA_OK;   // empty problem: nothing to compute
     if (!q || !k || !v || !o) return FA_ERR_NULL;
     const uintptr_t a = dtype == FA_BF16 ? 16 : 4;
@@ -119,6 +140,7 @@ fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, fl
     if (dtype != FA_BF16) return FA_ERR_DTYPE;
     if (d != 64 && d != 128) return FA_ERR_HEADDIM;
     if ((st = check_scale(scale)) != FA_OK) return st;
+    if (!fwd_grid_fits(B, Hq, N, FA_BF16)) return FA_ERR_SHAPE;
     if (B == 0 || N == 0) return FA_OK;
     if (!q || !k || !v || !o) return FA_ERR_NULL;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
@@ -141,6 +163,7 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
     if (dtype != FA_BF16) return FA_ERR_DTYPE;
     if (d != 64 && d != 128) return FA_ERR_HEADDIM;
     if ((st = check_scale(scale)) != FA_OK) return st;
+    if (!fwd_grid_fits(B, Hq, N, FA_BF16)) return FA_ERR_SHAPE;
     if (B == 0 || N == 0) return FA_OK;
     if (!q || !k || !v || !o || !block_mask) return FA_ERR_NULL;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
@@ -152,8 +175,8 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
     return launched(fa::launch_fwd_sparse_bf16(p, static_cast<hipStream_t>(stream)));
 }
 
-size_t fa_bwd_workspace_size(int B, int Hq, int N, int d) {
-    if (B < 0 || Hq <= 0 || N < 0 || d <= 0) return 0;
+size_t fa_bwd_workspace_size(int B, int Hq, int N) {
+    if (B < 0 || Hq <= 0 || N < 0) return 0;
     return (size_t)B * (size_t)Hq * (size_t)N * 2 * sizeof(float);
 }
 
@@ -164,8 +187,9 @@ static fa_status check_bwd_common(int B, int Hq, int Hkv, int N, int d, fa_dtype
     if (st != FA_OK) return st;
     if (dtype != FA_BF16) return FA_ERR_DTYPE;        // fp32 backward is not provided
     if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (!bwd_grid_fits(B, Hq, Hkv, N, d)) return FA_ERR_SHAPE;
     if (B == 0 || N == 0) return FA_OK;
-    if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, Hq, N, d)) return FA_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, Hq, N)) return FA_ERR_WORKSPACE;
     if (misaligned(workspace, 4)) return FA_ERR_ALIGN;
     return FA_OK;
 }
@@ -292,9 +316,11 @@ static fa_status check_splitkv_shape(int B, int Hq, int Hkv, int Nq, int Nk, int
         return FA_ERR_SHAPE;
     int splits, kps;
     splitkv_plan(B, Hq, Hkv, Nq, Nk, num_splits, &splits, &kps);
-    const long double rows = (long double)(Hq / Hkv) * Nq;
-    if ((long double)B * Hkv * ((rows + 31) / 32 + 1) * splits > 4.0e9L) return FA_ERR_SHAPE;
-    if ((long double)B * Hq * Nq > 4.0e9L) return FA_ERR_SHAPE;   // merge: one workgroup per row
+    const long long rows = (long long)(Hq / Hkv) * Nq;
+    // range kernel: (batch, kv-head, 32-row tile, range) workgroups of 256; merge: one
+    // workgroup of 256 per query row
+    if (!grid_fits((long double)B * Hkv * ((rows + 31) / 32) * splits, 256)) return FA_ERR_SHAPE;
+    if (!grid_fits((long double)B * Hq * Nq, 256)) return FA_ERR_SHAPE;
     return FA_OK;
 }
 

@@ -354,7 +354,7 @@ hipError_t launch_bwd_prep_bf16(const BwdParams& p, hipStream_t stream) {
 
 hipError_t launch_bwd_dkdv_bf16(const BwdParams& p, hipStream_t stream) {
     const int nkt = (p.N + kBK - 1) / kBK;
-    dim3 grid((unsigned)(nkt * p.Hkv * p.B)), block(kThreadsKV);
+    dim3 grid((unsigned)((long long)nkt * p.Hkv * p.B)), block(kThreadsKV);
     if (p.d == 128) {
         if (p.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), grid, block, 0, stream, p);

@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
 
 hipError_t launch_bwd_dq_bf16(const BwdParams& p, hipStream_t stream) {
     const int nqt = (p.N + kBR - 1) / kBR;
-    dim3 grid((unsigned)(nqt * p.Hq * p.B)), block(kThreads);
+    dim3 grid((unsigned)((long long)nqt * p.Hq * p.B)), block(kThreads);
     if (p.d == 128) {
         if (p.causal) hipLaunchKernelGGL((bwd_dq_kernel<128, true>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((bwd_dq_kernel<128, false>), grid, block, 0, stream, p);

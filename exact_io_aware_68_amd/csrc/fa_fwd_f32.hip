@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(FwdParams p) {
 
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream) {
     const int nqt = (p.N + kRows - 1) / kRows;
-    dim3 grid((unsigned)(nqt * p.Hq * p.B)), block(kRows);
+    dim3 grid((unsigned)((long long)nqt * p.Hq * p.B)), block(kRows);
     if (p.d <= 32) hipLaunchKernelGGL((fwd_f32_kernel<32>), grid, block, 0, stream, p);
     else if (p.d <= 64) hipLaunchKernelGGL((fwd_f32_kernel<64>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((fwd_f32_kernel<128>), grid, block, 0, stream, p);

@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sparse_bf16_kernel(FwdParams 
 
 hipError_t launch_fwd_sparse_bf16(const FwdParams& p, hipStream_t stream) {
     const int nqt = (p.N + kBR - 1) / kBR;
-    dim3 grid((unsigned)(nqt * p.Hq * p.B)), block(kThreads);
+    dim3 grid((unsigned)((long long)nqt * p.Hq * p.B)), block(kThreads);
     if (p.d == 128) {
         if (p.causal) hipLaunchKernelGGL((fwd_sparse_bf16_kernel<128, true>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((fwd_sparse_bf16_kernel<128, false>), grid, block, 0, stream, p);

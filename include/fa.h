@@ -52,12 +52,13 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = 1,      /* a required pointer is NULL                                      */
-    FA_ERR_SHAPE = 2,     /* B, Hq, Hkv or N negative, Hq or Hkv zero, or a size overflows    */
+    FA_ERR_SHAPE = 2,     /* B, Hq, Hkv or N negative, Hq or Hkv zero, a size overflows, or a
+                             launch would need 2^32 or more work-items in its grid            */
     FA_ERR_DTYPE = 3,     /* unknown dtype, or a dtype this entry point does not support      */
     FA_ERR_HEADDIM = 4,   /* d outside the supported set for the dtype                        */
     FA_ERR_GQA = 5,       /* Hq is not a multiple of Hkv                                      */
@@ -111,10 +112,10 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
 
 /*
  * Bytes of device workspace fa_bwd needs: two fp32 per query row (D_i = sum_c dO_ic O_ic and
- * the row's log-sum-exp in base 2), i.e. B * Hq * N * 8 — linear in N, never N^2.  Returns 0
- * for an invalid shape.
+ * the row's log-sum-exp in base 2), i.e. B * Hq * N * 8 — linear in N, never N^2, and
+ * independent of d.  Returns 0 for an invalid shape.
  */
-size_t fa_bwd_workspace_size(int B, int Hq, int N, int d);
+size_t fa_bwd_workspace_size(int B, int Hq, int N);
 
 /*
  * Backward by recomputation.  Inputs: q, k, v as in fa_fwd; o and lse exactly as fa_fwd wrote

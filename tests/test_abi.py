@@ -48,9 +48,38 @@ def test_status_strings(lib):
 
 
 def test_workspace_is_linear_in_N(lib):
-    assert fa.fa_bwd_workspace_size(2, 16, 4096, 128) == 2 * 16 * 4096 * 8
-    assert fa.fa_bwd_workspace_size(2, 16, 8192, 128) == 2 * fa.fa_bwd_workspace_size(2, 16, 4096, 128)
-    assert fa.fa_bwd_workspace_size(-1, 16, 8, 64) == 0
+    assert fa.fa_bwd_workspace_size(2, 16, 4096) == 2 * 16 * 4096 * 8
+    assert fa.fa_bwd_workspace_size(2, 16, 8192) == 2 * fa.fa_bwd_workspace_size(2, 16, 4096)
+    assert fa.fa_bwd_workspace_size(-1, 16, 8) == 0
+    assert fa.fa_bwd_workspace_size(1, 0, 8) == 0
+
+
+# Launch grids: HIP limits a 1-D grid to fewer than 2^32 work-items, so shapes whose grid would
+# reach that are FA_ERR_SHAPE on the host, never a failed launch.
+@pytest.mark.parametrize("call,code", [
+    # forward bf16: B * Hq * ceil(N / 128) workgroups of 256
+    (lambda lib: fwd(lib, B=1, Hq=16384, Hkv=1, N=128 * 1024, d=64), SHAPE),
+    (lambda lib: fwd(lib, B=2, Hq=8192, Hkv=1, N=128 * 1024, d=64), SHAPE),
+    # forward fp32: B * Hq * ceil(N / 64) workgroups of 64
+    (lambda lib: fwd(lib, B=1, Hq=1 << 20, Hkv=1, N=64 * 64, d=1, dtype=fa.FA_F32), SHAPE),
+    # window and block-sparse share the forward's grid
+    (lambda lib: win(lib, B=1, Hq=16384, Hkv=1, N=128 * 1024, d=64), SHAPE),
+    (lambda lib: bsp(lib, B=256, Hq=256, Hkv=1, N=65536, d=64), SHAPE),
+    # backward: dK/dV B * Hkv * ceil(N / 128) workgroups of 512
+    (lambda lib: bwd(lib, B=1, Hq=8192, Hkv=8192, N=128 * 1024, d=64), SHAPE),
+    # split-KV merge: one workgroup of 256 per query row
+    (lambda lib: skv(lib, B=1, Hq=1, Hkv=1, Nq=1 << 24, Nk=1), SHAPE),
+])
+def test_grids_past_2_32_work_items_are_shape_errors(lib, call, code):
+    assert call(lib) == code
+
+
+@pytest.mark.skipif("_gpu_present()", reason="fake pointers must never reach a real GPU")
+def test_grids_just_below_the_limit_pass_the_shape_checks(lib):
+    # 16384 * 1023 workgroups of 256 = 2^32 - 2^22 work-items: valid, so the call reaches the
+    # device check (no GPU in this process)
+    assert fwd(lib, B=1, Hq=16384, Hkv=1, N=128 * 1023, d=64) == DEVICE
+    assert skv(lib, B=1, Hq=1, Hkv=1, Nq=(1 << 24) - 1, Nk=1, wsb=1 << 40) == DEVICE
 
 
 def test_kernel_names(lib):

@@ -108,7 +108,7 @@ def test_stages_match_fa_bwd():
                        key_lens=x["key_lens"])
     whole = fa.fa_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, scale=x["scale"], causal=True,
                       key_lens=x["key_lens"])
-    ws = torch.empty(fa.fa_bwd_workspace_size(2, 4, 260, 128), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(fa.fa_bwd_workspace_size(2, 4, 260), dtype=torch.uint8, device=DEV)
     dq, dk, dv = (torch.empty_like(t) for t in whole)
     fa.fa_bwd_prep(o, x["do"], lse, ws)
     fa.fa_bwd_dkdv(x["q"], x["k"], x["v"], x["do"], dk, dv, ws, scale=x["scale"], causal=True,

@@ -42,7 +42,7 @@ def test_backward_outputs_and_workspace():
     qb, dq = guarded((B, Hq, N, d), torch.float32)
     kb, dk = guarded((B, Hkv, N, d), torch.float32)
     vb, dv = guarded((B, Hkv, N, d), torch.float32)
-    nws = fa.fa_bwd_workspace_size(B, Hq, N, d)
+    nws = fa.fa_bwd_workspace_size(B, Hq, N)
     wsb = torch.full((nws + 2 * G,), 0xFF, dtype=torch.uint8, device=DEV)
     ws = wsb[G:G + nws]
     fa.fa_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, scale=x["scale"], causal=True,
