@@ -120,6 +120,10 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
 
     const int q0 = qt * kBR + kWR * w;    // this wave's first query row; half h: q0 + 32h + c
     const float C = p.scale * kLog2e;
+    // Window instances: the last step (relative to kb) that holds some row's first visible key;
+    // the wave's last row starts latest.  With an unbounded left side every row sees key 0.
+    int jfresh = -1;
+    if constexpr (WIN) jfresh = wl >= 0 ? (max(q0 + kWR - 1 - wl, 0) - kb) / kBC : 0;
 
     // Q fragments: B operands of S^T = K Q^T, lane = query row, slots = 8 consecutive d.
     bf16x8 qf[NH][NS];
@@ -211,7 +215,12 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
     // rescaled, and the step's P is recomputed against it.  In real arithmetic the result does
     // not depend on the reference point, since O and l always share it; the cap keeps every P
     // and partial sum far from the fp32 and bf16 limits.  The common step computes no row max.
-    auto exponentiate = [&](const f32x16 (&st)[NH][kNT], bf16x8 (&pf)[NH][kNT][2]) {
+    auto exponentiate = [&](int j, const f32x16 (&st)[NH][kNT], bf16x8 (&pf)[NH][kNT][2]) {
+        // Window instances: a row may see no key in the workgroup's first steps, so its
+        // reference point starts unset (-inf) and, until every row of the wave has met its first
+        // visible key (steps up to jfresh), each step moves it to the row max so far.  A
+        // placeholder point would let exponentials of very negative scores underflow to zero.
+        const bool fresh = WIN && j <= jfresh;
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
             float pe[kNT][16];
@@ -227,8 +236,12 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
                         rs += pe[t][r];
                     }
             };
-            expo();
-            if (__builtin_amdgcn_ballot_w64(!(rs <= kSumCap)) != 0) {
+            bool move = fresh;
+            if (!fresh) {
+                expo();
+                move = __builtin_amdgcn_ballot_w64(!(rs <= kSumCap)) != 0;
+            }
+            if (move) {
                 float mx = kNegInf;
 #pragma unroll
                 for (int t = 0; t < kNT; ++t)
@@ -302,18 +315,20 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
     if (ntiles > 0) {
         scores(ksub(0), sa);
         if (need_mask(0)) mask(0, sa);
-        // The reference point starts at the row max of the first step, or at 0 for a row that
-        // sees no key of it (possible with a window or a short key length): it is a reference
-        // point, never -inf, so every later rescale is a finite factor.
+        // Without a window every row sees key 0 in step 0, so the reference point starts at
+        // step 0's row max (finite: every later rescale is a finite factor).  Window instances
+        // leave it unset; their first steps set it (see exponentiate).
+        if constexpr (!WIN) {
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            float mx = kNegInf;
+            for (int h = 0; h < NH; ++h) {
+                float mx = kNegInf;
 #pragma unroll
-            for (int t = 0; t < kNT; ++t)
+                for (int t = 0; t < kNT; ++t)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[h][t][r]);
-            mx = max_with_partner(mx) * C;
-            m[h] = mx == kNegInf ? 0.f : mx;
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[h][t][r]);
+                mx = max_with_partner(mx) * C;
+                m[h] = mx == kNegInf ? 0.f : mx;
+            }
         }
     }
     __syncthreads();   // keys 0..31 in buffer 1 are overwritten by K tile 1 during steps 0, 1
@@ -330,7 +345,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
             if (T + 1 < nlt) load_v(T + 1, tb ^ 1);
         }
         scores(sm.k[tb] + half * kBC * D, nxt);             // MFMA (= ksub(j + 1)) ...
-        exponentiate(cur, pf);                              // ... alongside VALU
+        exponentiate(j, cur, pf);                           // ... alongside VALU
         if constexpr (decltype(maskn)::value) mask(j + 1, nxt);
         pv(sm.v[tb] + half * kBC * D, pf);                  // (= vsub(j))
         if constexpr (decltype(odd)::value) {
@@ -387,10 +402,10 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
     }
     if (j + 1 < ntiles) {
         step(Flag<true>{}, Flag<false>{}, Phase<-1>{}, j, sa, sb);   // no loads left: none issued
-        exponentiate(sb, pf);
+        exponentiate(j + 1, sb, pf);
         pv(vsub(j + 1), pf);
     } else if (j < ntiles) {
-        exponentiate(sa, pf);
+        exponentiate(j, sa, pf);
         pv(vsub(j), pf);
     }
 
@@ -434,7 +449,7 @@ constexpr int kNH = 1;
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
     constexpr int kBR = rows_per_block<kNH>();
     const int nqt = (p.N + kBR - 1) / kBR;
-    dim3 grid((unsigned)(nqt * p.Hq * p.B)), block(kThreads);
+    dim3 grid((unsigned)((long long)nqt * p.Hq * p.B)), block(kThreads);
     if (p.d == 128) {
         if (p.causal)
             hipLaunchKernelGGL((fwd_bf16_kernel<128, true, kNH>), grid, block, 0, stream, p);
@@ -453,7 +468,7 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
 hipError_t launch_fwd_window_bf16(const FwdParams& p, hipStream_t stream) {
     constexpr int kBR = rows_per_block<kNH>();
     const int nqt = (p.N + kBR - 1) / kBR;
-    dim3 grid((unsigned)(nqt * p.Hq * p.B)), block(kThreads);
+    dim3 grid((unsigned)((long long)nqt * p.Hq * p.B)), block(kThreads);
     if (p.d == 128)
         hipLaunchKernelGGL((fwd_window_bf16_kernel<128, kNH>), grid, block, 0, stream, p);
     else

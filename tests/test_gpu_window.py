@@ -93,3 +93,29 @@ def test_window_workload_sampled_rows():
     idx = tuple(torch.tensor(a) for a in zip(*picks))
     check_close("O", np64(o[idx]), O, TOL_BF16_MAX, TOL_BF16_MEAN)
     check_close("LSE", np64(lse[idx]), LSE, TOL_LSE)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("window,padded", [((3, 3), False), ((40, 5), True), ((0, 70), False)])
+def test_very_negative_logits(d, window, padded):
+    """Every scaled logit near -150 in log2 units (K close to -Q): exponentials taken against
+    any reference point other than a visible score's would underflow fp32.  With a small left
+    window most rows see no key in their workgroup's first steps, so the kernel must set each
+    row's reference point from the first key that row actually sees."""
+    B, Hq, Hkv, N = 2, 2, 1, 700
+    print(f"\nwindow very negative logits d={d} window={window} padded={padded}", flush=True)
+    scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    a = (150.0 / (scale * 1.4426950408889634 * d)) ** 0.5
+    g = torch.Generator().manual_seed(91 + d + window[0])
+    q = (a + 0.1 * a * torch.randn(B, Hq, N, d, generator=g)).to(torch.bfloat16)
+    k = (-a + 0.1 * a * torch.randn(B, Hkv, N, d, generator=g)).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16)
+    kl = torch.tensor([N, 451], dtype=torch.int32) if padded else None
+    x = {"q": q, "k": k, "v": v, "scale": scale, "key_lens": kl}
+    o, lse = run(x, window)
+    O, LSE = attn_fwd(q, k, v, scale, False, kl, window=window)
+    rows = np.isfinite(LSE)
+    assert np.median(LSE[rows]) < -90.0   # natural log: the logits really sit near -150 log2 units
+    check_close("O", np64(o), O, TOL_BF16_MAX, TOL_BF16_MEAN)
+    check_close("LSE", np64(lse)[rows], LSE[rows], TOL_LSE)
+    assert np.all(np.isneginf(np64(lse)[~rows])) and np.all(np64(o)[~rows] == 0)
