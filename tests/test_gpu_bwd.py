@@ -5,7 +5,7 @@ import torch
 
 import exact_io_aware_68_amd as fa
 import fa_inputs as fi
-from oracle import attn_bwd, attn_bwd_heads, attn_dq_rows, attn_fwd
+from oracle import attn_bwd, attn_dq_rows, attn_fwd
 from tests._parity import TOL_BF16_MAX, TOL_BF16_MEAN, check_close, np64
 
 pytestmark = pytest.mark.gpu
@@ -141,27 +141,6 @@ def test_side_stream_gives_the_same_results():
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
     for a, b, c in zip(ref, got1, got2):
         assert torch.equal(a, b) and torch.equal(a, c)
-
-
-def test_c5_full_size_sampled_heads():
-    """The backward workload at full size, in the bench's launch configuration; three whole
-    kv-heads checked against the oracle, gradient invariants checked on every head."""
-    w = fi.WORKLOADS["c5"]
-    print(f"\nfull-size c5: B={w.B} H={w.Hq} N={w.N} d={w.d}", flush=True)
-    x = fi.make(w)
-    dq, dk, dv = run_fwd_bwd(x, True)
-    for t in (dq, dk, dv):
-        assert torch.isfinite(t).all()
-    picks = [(0, 0), (1, 7), (1, 15)]
-    ref = attn_bwd_heads(x["q"], x["k"], x["v"], x["do"], x["scale"], True, None, picks)
-    for (b, g), (rq, rk, rv) in ref.items():
-        check_close("dQ", np64(dq[b, g]), rq[0], TOL_BF16_MAX, TOL_BF16_MEAN)
-        check_close("dK", np64(dk[b, g]), rk, TOL_BF16_MAX, TOL_BF16_MEAN)
-        check_close("dV", np64(dv[b, g]), rv, TOL_BF16_MAX, TOL_BF16_MEAN)
-    # every head: sum_j dV_j = sum_i dO_i (rows of P sum to one)
-    sdv = dv.double().sum(2).cpu()
-    sdo = x["do"].double().sum(2)
-    assert (sdv - sdo).abs().max().item() < 0.5
 
 
 def test_backward_tensors_past_2_31_elements():

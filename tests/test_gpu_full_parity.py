@@ -1,0 +1,111 @@
+"""Whole-tensor parity of the full-size workloads against the fp64 oracle, in the launch
+configuration the bench times.
+
+The pages claim exactness: the result equals exact standard attention (tutorial page "Flash
+attention and efficient attention", Worked example; study-note page "FlashAttention paper",
+Exact, not approximate).  So every row of the bf16 workloads is compared with the oracle:
+  - c2 (B=4 H=16 N=2048 d=64, non-causal): O and LSE of all 64 heads;
+  - c3 (B=2 H=16 N=8192 d=128, causal): O and LSE of all 32 heads;
+  - c5 (B=2 H=16 N=4096 d=128, causal backward): dQ, dK, dV of all 32 heads;
+  - c4 (B=4 Hq=32 Hkv=8 N=16384 d=128, causal, key lengths): a stated subset of 32 q-heads,
+    one per (batch, kv-group): q-head g*4 + (b + g) % 4 of kv-group g in batch b, so every batch
+    (every key length), every kv-group and every position inside a group is covered.  The other
+    rows of c4 are checked on samples (tests/test_gpu_fwd.py).
+max-abs and mean-abs are taken over every checked element of each tensor.  The oracle runs head
+by head on a pool of host threads.
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_68_amd as fa
+import fa_inputs as fi
+from oracle import attn_bwd, attn_fwd
+from tests._parity import TOL_BF16_MAX, TOL_BF16_MEAN, TOL_LSE, Agg, np64, oracle_map
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def c4_heads(w):
+    G = w.Hq // w.Hkv
+    return [(b, g * G + (b + g) % G) for b in range(w.B) for g in range(w.Hkv)]
+
+
+def forward_full(name, heads=None):
+    w = fi.WORKLOADS[name]
+    x = fi.make(w)
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    kl = None if x["key_lens"] is None else x["key_lens"].to(DEV)
+    o, lse = fa.fa_fwd(q, k, v, scale=x["scale"], causal=w.causal, key_lens=kl)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    G = w.Hq // w.Hkv
+    heads = heads or [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    lens = None if x["key_lens"] is None else x["key_lens"].tolist()
+
+    def ref(bh):
+        b, h = bh
+        g = h // G
+        return attn_fwd(x["q"][b:b + 1, h:h + 1], x["k"][b:b + 1, g:g + 1],
+                        x["v"][b:b + 1, g:g + 1], x["scale"], w.causal,
+                        None if lens is None else [lens[b]])
+
+    ao, al = Agg("O", TOL_BF16_MAX, TOL_BF16_MEAN), Agg("LSE", TOL_LSE)
+    t0 = time.time()
+    for (b, h), (O, LSE) in zip(heads, oracle_map(ref, heads)):
+        ao.add(np64(o[b, h]), O[0, 0])
+        al.add(np64(lse[b, h]), LSE[0, 0])
+    (om, omean), (lm, _) = ao.check(), al.check()
+    print(f"\n{name}: {len(heads)} heads, {ao.n} O elements; O max {om:.3g} mean {omean:.3g}, "
+          f"LSE max {lm:.3g} (oracle {time.time() - t0:.1f} s)", flush=True)
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_forward_every_row(name):
+    w = fi.WORKLOADS[name]
+    print(f"\nfull parity {name}: B={w.B} Hq={w.Hq} N={w.N} d={w.d} causal={w.causal}", flush=True)
+    forward_full(name)
+
+
+def test_c4_forward_head_subset():
+    w = fi.WORKLOADS["c4"]
+    heads = c4_heads(w)
+    assert {b for b, _ in heads} == set(range(w.B))
+    assert {(b, h // (w.Hq // w.Hkv)) for b, h in heads} == {(b, g) for b in range(w.B)
+                                                             for g in range(w.Hkv)}
+    assert {h % (w.Hq // w.Hkv) for _, h in heads} == set(range(w.Hq // w.Hkv))
+    print(f"\nfull parity c4: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d}, "
+          f"{len(heads)} q-heads", flush=True)
+    forward_full("c4", heads)
+
+
+def test_c5_backward_every_row():
+    w = fi.WORKLOADS["c5"]
+    print(f"\nfull parity c5 backward: B={w.B} H={w.Hq} N={w.N} d={w.d}", flush=True)
+    x = fi.make(w)
+    g = {n: x[n].to(DEV) for n in ("q", "k", "v", "do")}
+    o, lse = fa.fa_fwd(g["q"], g["k"], g["v"], scale=x["scale"], causal=True)
+    dq, dk, dv = fa.fa_bwd(g["q"], g["k"], g["v"], o, g["do"], lse, scale=x["scale"], causal=True)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    G = w.Hq // w.Hkv
+    kv = [(b, kh) for b in range(w.B) for kh in range(w.Hkv)]
+
+    def ref(bk):
+        b, kh = bk
+        sl = slice(kh * G, (kh + 1) * G)
+        return attn_bwd(x["q"][b:b + 1, sl], x["k"][b:b + 1, kh:kh + 1],
+                        x["v"][b:b + 1, kh:kh + 1], x["do"][b:b + 1, sl], x["scale"], True)
+
+    aq, ak, av = (Agg(n, TOL_BF16_MAX, TOL_BF16_MEAN) for n in ("dQ", "dK", "dV"))
+    t0 = time.time()
+    for (b, kh), (rq, rk, rv) in zip(kv, oracle_map(ref, kv)):
+        aq.add(np64(dq[b, kh * G:(kh + 1) * G]), rq[0])
+        ak.add(np64(dk[b, kh]), rk[0, 0])
+        av.add(np64(dv[b, kh]), rv[0, 0])
+    res = {a.name: a.check() for a in (aq, ak, av)}
+    print("c5: " + ", ".join(f"{n} max {m:.3g} mean {e:.3g}" for n, (m, e) in res.items())
+          + f" (oracle {time.time() - t0:.1f} s)", flush=True)

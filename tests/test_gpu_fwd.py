@@ -177,11 +177,11 @@ def _sample_rows(w, n_rand, seed):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+@pytest.mark.parametrize("name", ["c4"])
 def test_full_size_workload_sampled_rows(name):
-    """Full-size workloads in the launch configuration the bench times; the oracle recomputes
-    sampled rows one by one (first, last, tile edges, random) and every row is checked for
-    finiteness."""
+    """Rows of every q-head of the largest workload, beyond the head subset that
+    tests/test_gpu_full_parity.py checks in full: the oracle recomputes sampled rows one by one
+    (first, last, tile edges, random) and every row is checked for finiteness."""
     w = fi.WORKLOADS[name]
     print(f"\nfull-size {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d}", flush=True)
     x = fi.make(w)
@@ -219,14 +219,3 @@ def test_tensors_past_2_31_elements():
     check_close("LSE", np64(lse[idx]), LSE, TOL_LSE)
     del x, o, lse
     torch.cuda.empty_cache()
-
-
-def test_c2_two_heads_in_full():
-    w = fi.WORKLOADS["c2"]
-    x = fi.make(w)
-    o, lse = run_fwd(x, False)
-    heads = [(0, 0), (3, 15)]
-    O, LSE = attn_fwd(x["q"], x["k"], x["v"], x["scale"], False, None, heads=heads)
-    for b, h in heads:
-        check_close("O", np64(o[b, h]), O[b, h], TOL_BF16_MAX, TOL_BF16_MEAN)
-        check_close("LSE", np64(lse[b, h]), LSE[b, h], TOL_LSE)
