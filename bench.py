@@ -303,30 +303,6 @@ def cpu_baseline(x, w, budget_s=20.0):
                       f"host affinity {len(os.sched_getaffinity(0))} cpus"}
 
 
-def sclk_sample(n=5, gap_s=0.004):
-    """The shader clock the driver reports for device 0 (its pp_dpm_sclk file: the line marked
-    '*' is the current level), read n times gap_s apart.  Called while queued steps run."""
-    import re
-
-    import torch
-    try:
-        pr = torch.cuda.get_device_properties(0)
-        path = (f"/sys/bus/pci/devices/{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:"
-                f"{pr.pci_device_id:02x}.0/pp_dpm_sclk")
-        vals = []
-        for _ in range(n):
-            with open(path) as f:
-                for ln in f:
-                    m = re.search(r"(\d+)\s*[Mm][Hh][Zz]", ln) if "*" in ln else None
-                    if m:
-                        vals.append(int(m.group(1)))
-            time.sleep(gap_s)
-        return {"samples": vals, "median": sorted(vals)[len(vals) // 2] if vals else None,
-                "source": path}
-    except Exception as e:   # no such file on this system: report why, measure nothing
-        return {"samples": [], "median": None, "source": f"unavailable ({type(e).__name__})"}
-
-
 def copy_calibration(nbytes=1 << 30, reps=5):
     """A plain device copy of known size for counter calibration (reads and writes nbytes)."""
     import torch
@@ -345,11 +321,94 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 TRAFFIC_CMD = """    cd /tmp && export TMPDIR=/tmp
     for C in FETCH_SIZE WRITE_SIZE; do
       rocprofv3 --pmc $C -T -f csv -d $OUT/pmc -o bench_$C -- \\
-          python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline --cold-steps 0
+          python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline --cold-steps 0 --no-other-configs
       rocprofv3 --pmc $C -T -f csv -d $OUT/pmc -o copy_$C -- \\
           python3 $REPO/bench.py --copy-calib
     done
     python3 $REPO/bench.py --traffic-summary $OUT/pmc"""
+
+def causal_pairs(N, L):
+    """Visible (query, key) pairs of one causal head whose keys stop at L: row i sees
+    min(i + 1, L) keys."""
+    L = min(L, N)
+    return L * (L + 1) // 2 + (N - L) * L
+
+
+def time_launches(fn, reps=10, warmup=3):
+    """Mean duration (ms) of fn's launches, HIP events on the current stream around each."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+
+
+def other_configs(reps=10):
+    """The other bf16 workloads, each timed on its own (after the timed steps, outside them):
+    c2 and c4 forwards, c5 forward and backward (prep + dK/dV + dQ).  c4's work is given both by
+    the formula (4 N^2 d B H / 2, counting keys past each key length) and on the visible pairs."""
+    import torch
+
+    import exact_io_aware_68_amd as fa
+    import fa_inputs as fi
+    dev = "cuda:0"
+    res = {}
+    for name in ("c2", "c4", "c5"):
+        w = fi.WORKLOADS[name]
+        x = fi.make(w, want_do=name == "c5")
+        q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+        kl = None if x["key_lens"] is None else x["key_lens"].to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+        sc = x["scale"]
+
+        def fwd():
+            fa.fa_fwd(q, k, v, scale=sc, causal=w.causal, key_lens=kl, o=o, lse=lse)
+
+        ms = time_launches(fwd, reps)
+        ff = fwd_flops(w.B, w.Hq, w.N, w.d, w.causal)
+        r = {"workload": f"B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} causal={w.causal} "
+                         f"key_lens={x['key_lens'].tolist() if w.padded else 'none'}",
+             "fwd_ms": round(ms, 4), "fwd_flops": ff,
+             "fwd_tflops": round(ff / (ms * 1e-3) / 1e12, 2),
+             "fwd_pct_peak": round(100 * ff / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        if w.padded:
+            pairs = sum(causal_pairs(w.N, int(L)) for L in x["key_lens"].tolist()) * w.Hq
+            fv = 4.0 * w.d * pairs
+            r.update(fwd_flops_visible_pairs=fv,
+                     fwd_tflops_visible_pairs=round(fv / (ms * 1e-3) / 1e12, 2))
+        if name == "c5":
+            fa.fa_fwd(q, k, v, scale=sc, causal=w.causal, key_lens=kl, o=o, lse=lse)
+            do = x["do"].to(dev)
+            dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+            dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+            dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+            ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.Hq, w.N), dtype=torch.uint8,
+                             device=dev)
+
+            def bwd():
+                fa.fa_bwd(q, k, v, o, do, lse, scale=sc, causal=w.causal, key_lens=kl, dq=dq,
+                          dk=dk, dv=dv, workspace=ws)
+
+            bms = time_launches(bwd, reps)
+            bf = bwd_flops(w.B, w.Hq, w.N, w.d, w.causal)
+            r.update(bwd_ms=round(bms, 4), bwd_flops=bf,
+                     bwd_tflops=round(bf / (bms * 1e-3) / 1e12, 2),
+                     bwd_pct_peak=round(100 * bf / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2))
+        res[name] = r
+        del x, q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return res
+
 
 def bench_decode(args):
     """Split-KV decode forward on a decode workload: one step = one fa_fwd_splitkv call (the range
@@ -590,9 +649,8 @@ def main():
                     help="steps timed kernel by kernel after a 512 MiB cache-evicting read "
                          "(reported as kernels_ms_cold_cache; 0 for profiling runs)")
     ap.add_argument("--flush-mib", type=int, default=512, help=argparse.SUPPRESS)
-    ap.add_argument("--sclk-steps", type=int, default=30,
-                    help="steps queued after the timed ones while the shader clock is read "
-                         "(0: no clock reading)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the event-timed launches of the other workloads (c2, c4, c5)")
     ap.add_argument("--splits", type=int, default=0,
                     help="decode workloads: number of key ranges (0: the library's choice)")
     ap.add_argument("--copy-calib", action="store_true")
@@ -684,15 +742,6 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     kern_ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in names}
-    # The shader clock under this load: more steps are queued (outside the timed region) and
-    # the driver's current clock is read while the GPU runs them.
-    sclk = None
-    if args.sclk_steps > 0:
-        for _ in range(args.sclk_steps):
-            step(False)
-        time.sleep(0.005)
-        sclk = sclk_sample()
-        torch.cuda.synchronize()
     # Per-kernel times with cold caches: each launch follows a 512 MiB read that evicts L2 and
     # the Infinity Cache (after the timed steps, with the clocks already up; profiling runs pass
     # --cold-steps 0, so their last dispatches are the timed steps).
@@ -764,9 +813,13 @@ def main():
             "measured_bytes": {n: stored_traffic(n, args.workload)
                                for n in ("bwd_prep", "bwd_dkdv", "bwd_dq")}},
         "roofline": roof,
-        "sclk_mhz_under_load": sclk,
+        "other_configs": None,
         "cpu_baseline": None,
     }
+    if args.workload == "c3" and not args.no_other_configs:
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+        out["other_configs"] = other_configs()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, w)
     print(json.dumps(out), flush=True)
