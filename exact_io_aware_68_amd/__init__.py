@@ -9,6 +9,7 @@ The functions carry the C names (see include/fa.h for the full contract):
 
     fa_fwd(q, k, v, *, scale, causal, key_lens, o, lse)              -> (o, lse)
     fa_bwd(q, k, v, o, dO, lse, *, scale, causal, key_lens, ...)     -> (dq, dk, dv)
+    fa_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, *, ...)          (fa_bwd, no allocation)
     fa_bwd_prep(o, dO, lse, workspace), fa_bwd_dkdv(q, k, v, dO, dk, dv, workspace, ...),
     fa_bwd_dq(q, k, v, dO, dq, workspace, ...)                       (the stages of fa_bwd)
     fa_bwd_workspace_size, fa_fwd_kernel_name, fa_bwd_dkdv_kernel_name, fa_bwd_dq_kernel_name,
@@ -33,10 +34,11 @@ __all__ = [
     "fa_bwd_workspace_size", "fa_fwd_kernel_name", "fa_bwd_dkdv_kernel_name",
     "fa_bwd_dq_kernel_name", "fa_status_str", "fa_abi_version", "FA_F32", "FA_BF16",
     "fa_fwd_splitkv", "fa_fwd_splitkv_splits", "fa_fwd_splitkv_workspace_size", "fa_fwd_window",
-    "fa_fwd_blocksparse", "BLOCK_Q", "BLOCK_K",
+    "fa_fwd_blocksparse", "BLOCK_Q", "BLOCK_K", "fa_bwd_noalloc", "NOALLOC_MAX_ROWS",
 ]
 
 BLOCK_Q, BLOCK_K = 128, 64   # block-sparse bitmap granularity (query rows, keys)
+NOALLOC_MAX_ROWS = 4194304   # FA_NOALLOC_MAX_ROWS: B * Hq * N limit of fa_bwd_noalloc
 
 FA_F32, FA_BF16 = 0, 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +69,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd.restype = I
     lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, Z, I, I, I, I, I, F, I, I, P]
     lib.fa_bwd.restype = I
+    lib.fa_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.fa_bwd_noalloc.restype = I
     lib.fa_bwd_prep.argtypes = [P, P, P, P, Z, I, I, I, I, I, P]
     lib.fa_bwd_prep.restype = I
     lib.fa_bwd_dkdv.argtypes = [P, P, P, P, P, P, P, P, Z, I, I, I, I, I, F, I, I, P]
@@ -367,6 +371,25 @@ def fa_bwd(q, k, v, o, dO, lse, *, scale: float | None = None, causal: bool = Fa
                        int(causal), _dtype_code(q), _stream(stream, q.device))
     _check("fa_bwd", st)
     return dq, dk, dv
+
+
+def fa_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, *, scale: float | None = None,
+                   causal: bool = False, key_lens=None, stream=None):
+    """fa_bwd without a workspace and without any allocation, neither in the library nor here:
+    the caller passes every output (fp32 dq like q, dk and dv like k).  The per-row statistics
+    live in the library's fixed device scratch (B * Hq * N <= NOALLOC_MAX_ROWS); calls that may
+    overlap in time on one GPU race on it."""
+    fn = "fa_bwd_noalloc"
+    B, Hq, Hkv, N, d = _qkv(fn, q, k, v, key_lens)
+    _grad_inputs(fn, q, dO, o, lse)
+    _need(dq is not None and dk is not None and dv is not None, fn, "dq, dk and dv are required")
+    _grad_outputs(fn, q, k, dq, dk, dv)
+    _on_one_gpu(fn, q, k, v, o, dO, lse, key_lens, dq, dk, dv)
+    st = load().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+                               _ptr(key_lens), _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d,
+                               ctypes.c_float(_default_scale(d) if scale is None else scale),
+                               int(causal), _dtype_code(q), _stream(stream, q.device))
+    _check(fn, st)
 
 
 def fa_fwd_splitkv_splits(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, num_splits: int = 0) -> int:

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_launch.h"
 
@@ -75,6 +77,8 @@ const char* fa_status_str(int s) {
         case FA_ERR_WORKSPACE: return "workspace missing or too small";
         case FA_ERR_DEVICE: return "no HIP device available";
         case FA_ERR_LAUNCH: return "kernel launch failed";
+        case FA_ERR_TOO_LARGE:
+            return "problem larger than the fixed device scratch of this entry point";
         default: return "unknown status";
     }
 }
@@ -282,6 +286,80 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
     if ((st = device_ready()) != FA_OK) return st;
     fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, key_lens, dq, dk, dv, workspace, B, Hq,
                                  Hkv, N, d, scale, causal);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = launched(fa::launch_bwd_prep_bf16(p, s))) != FA_OK) return st;
+    if ((st = launched(fa::launch_bwd_dkdv_bf16(p, s))) != FA_OK) return st;
+    return launched(fa::launch_bwd_dq_bf16(p, s));
+}
+
+// ---- backward without allocation ------------------------------------------------------------
+//
+// fa_bwd_noalloc keeps fa_bwd's per-row statistics (D and the base-2 LSE, two fp32 per query
+// row) in a file-scope device array instead of a caller-supplied workspace.  In host code the
+// array's name is only a host-side stand-in: its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is ever passed on.
+
+}  // extern "C"
+
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)FA_NOALLOC_MAX_ROWS * 2 * sizeof(float);
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, once looked up
+
+// The current device's copy of `scratch`, or nullptr if the lookup failed.
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        scratch_ptr[dev] = ptr;
+    }
+    return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dO, const float* lse, const int32_t* key_lens, float* dq,
+                         float* dk, float* dv, int B, int Hq, int Hkv, int N, int d, float scale,
+                         int causal, fa_dtype dtype, void* stream) {
+    // Everything fa_bwd checks, with the fixed scratch standing in for the workspace (a
+    // non-null, suitably aligned placeholder: it is never dereferenced on the host).
+    const void* ws_check = reinterpret_cast<const void*>(uintptr_t{256});
+    if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_DTYPE;
+    fa_status st = check_shape(B, Hq, Hkv, N, d);
+    if (st != FA_OK) return st;
+    if ((long double)B * Hq * N > (long double)FA_NOALLOC_MAX_ROWS) return FA_ERR_TOO_LARGE;
+    if ((st = validate_grad(q, k, v, dO, key_lens, dk, dv, ws_check, kScratchBytes, B, Hq, Hkv,
+                            N, d, scale, dtype)) != FA_OK)
+        return st;
+    if (B == 0 || N == 0) return FA_OK;
+    if ((st = validate_grad(q, k, v, dO, key_lens, dq, dq, ws_check, kScratchBytes, B, Hq, Hkv,
+                            N, d, scale, dtype)) != FA_OK)
+        return st;
+    if ((st = validate_prep(o, dO, lse, ws_check, kScratchBytes, B, Hq, N, d, dtype)) != FA_OK)
+        return st;
+    if ((st = device_ready()) != FA_OK) return st;
+    void* ws = device_scratch();
+    if (!ws) return FA_ERR_DEVICE;
+    // The prep stage writes both statistics of every row of this problem before the two
+    // gradient stages read them, so nothing left in the scratch by an earlier call is read.
+    fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, key_lens, dq, dk, dv, ws, B, Hq, Hkv, N, d,
+                                 scale, causal);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = launched(fa::launch_bwd_prep_bf16(p, s))) != FA_OK) return st;
     if ((st = launched(fa::launch_bwd_dkdv_bf16(p, s))) != FA_OK) return st;

@@ -22,7 +22,8 @@
  *   lse      : [B][Hq][N] fp32      key_lens : [B] int32
  *   dq       : [B][Hq][N][d] fp32   dk, dv : [B][Hkv][N][d] fp32 (summed over each group)
  * All pointers are DEVICE pointers on the current HIP device, owned by the caller.  The library
- * allocates no memory and keeps no mutable global state; calls are reentrant.
+ * allocates no memory.  It keeps no mutable global state, with one exception: fa_bwd_noalloc's
+ * fixed scratch array (see there).  All other calls are reentrant.
  *
  * Ordering: every call enqueues its kernels on `stream` (a hipStream_t passed as void*; NULL is
  * the default stream) and returns without waiting.  Kernel faults surface at the caller's next
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
 typedef enum {
     FA_OK = 0,
@@ -66,7 +67,8 @@ typedef enum {
     FA_ERR_ALIGN = 7,     /* a pointer is misaligned                                          */
     FA_ERR_WORKSPACE = 8, /* workspace missing or smaller than fa_bwd_workspace_size()        */
     FA_ERR_DEVICE = 9,    /* no HIP device available                                          */
-    FA_ERR_LAUNCH = 10    /* the kernel launch failed                                         */
+    FA_ERR_LAUNCH = 10,   /* the kernel launch failed                                         */
+    FA_ERR_TOO_LARGE = 11 /* fa_bwd_noalloc: more rows than its fixed scratch holds            */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
@@ -131,6 +133,25 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  const float* lse, const int32_t* key_lens, float* dq, float* dk, float* dv,
                  void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
                  float scale, int causal, fa_dtype dtype, void* stream);
+
+/*
+ * fa_bwd for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, results and errors as fa_bwd
+ * without the workspace: the per-row statistics live in a fixed device array inside the library
+ * (FA_NOALLOC_MAX_ROWS rows of two fp32, 32 MiB, held on each GPU the library runs on until the
+ * process ends).  The call allocates nothing (no hipMalloc, no library allocation); the caller
+ * still owns every input and output.  B * Hq * N above FA_NOALLOC_MAX_ROWS is FA_ERR_TOO_LARGE.
+ * Every call on one GPU shares that GPU's array: calls that may overlap in time on one GPU (on
+ * different streams, or from different threads without ordering) race and must not be issued.
+ * Nothing in the array needs to start at zero: each call writes the statistics of all its rows
+ * before reading any.  The array's device address is looked up on the first call on each device
+ * (FA_ERR_DEVICE if that fails).
+ */
+#define FA_NOALLOC_MAX_ROWS 4194304
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dO, const float* lse, const int32_t* key_lens, float* dq,
+                         float* dk, float* dv, int B, int Hq, int Hkv, int N, int d, float scale,
+                         int causal, fa_dtype dtype, void* stream);
 
 /*
  * First stage of fa_bwd: writes D_i = sum_c dO_ic O_ic and LSE_i * log2(e) (fp32; +inf for a

@@ -11,7 +11,7 @@ import exact_io_aware_68_amd as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
-OK, NULL, SHAPE, DTYPE, HEADDIM, GQA, SCALE, ALIGN, WORKSPACE, DEVICE, LAUNCH = range(11)
+OK, NULL, SHAPE, DTYPE, HEADDIM, GQA, SCALE, ALIGN, WORKSPACE, DEVICE, LAUNCH, TOO_LARGE = range(12)
 A = 0x10000            # a 16-byte-aligned fake device address (never dereferenced here)
 
 
@@ -42,7 +42,7 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings(lib):
-    for s in range(11):
+    for s in range(12):
         assert fa.fa_status_str(s) and fa.fa_status_str(s) != "unknown status"
     assert fa.fa_status_str(99) == "unknown status"
 
@@ -133,6 +133,30 @@ def bwd(lib, q=A, k=A, v=A, o=A, do=A, lse=A, kl=None, dq=A, dk=A, dv=A, ws=A, w
 ])
 def test_bwd_argument_errors_before_any_hip_call(lib, kw, code):
     assert bwd(lib, **kw) == code
+
+
+def noalloc(lib, q=A, k=A, v=A, o=A, do=A, lse=A, kl=None, dq=A, dk=A, dv=A, B=1, Hq=2, Hkv=1,
+            N=8, d=128, scale=0.1, causal=1, dtype=fa.FA_BF16):
+    return lib.fa_bwd_noalloc(q, k, v, o, do, lse, kl, dq, dk, dv, B, Hq, Hkv, N, d,
+                              ctypes.c_float(scale), causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=1, Hq=64, Hkv=1, N=65537, d=64), TOO_LARGE),          # 4194368 rows > 4194304
+    (dict(B=2, Hq=32, Hkv=8, N=65536 + 1, d=128), TOO_LARGE),
+    (dict(dtype=fa.FA_F32), DTYPE), (dict(dtype=3), DTYPE), (dict(d=96), HEADDIM),
+    (dict(Hq=4, Hkv=3), GQA), (dict(N=-1), SHAPE), (dict(scale=float("nan")), SCALE),
+    (dict(do=None), NULL), (dict(lse=None), NULL), (dict(dq=None), NULL), (dict(dv=None), NULL),
+    (dict(dq=A + 4), ALIGN), (dict(o=A + 8), ALIGN), (dict(kl=A + 2), ALIGN),
+    (dict(B=0), OK), (dict(N=0, q=None), OK),
+])
+def test_noalloc_argument_errors_before_any_hip_call(lib, kw, code):
+    assert noalloc(lib, **kw) == code
+
+
+@pytest.mark.skipif("_gpu_present()", reason="fake pointers must never reach a real GPU")
+def test_noalloc_largest_problem_passes_the_checks(lib):
+    assert noalloc(lib, B=1, Hq=64, Hkv=1, N=65536, d=64) == DEVICE      # exactly 2^22 rows
 
 
 def test_bwd_stage_argument_errors(lib):
@@ -230,6 +254,7 @@ def _gpu_present():
 def test_valid_call_without_device_reports_device_error(lib):
     assert fwd(lib) == DEVICE
     assert bwd(lib) == DEVICE
+    assert noalloc(lib) == DEVICE
     assert skv(lib) == DEVICE
     assert win(lib) == DEVICE
     assert bsp(lib) == DEVICE
