@@ -39,9 +39,9 @@ struct BwdParams {
 };
 
 // Split-KV forward for decode shapes: Nq query rows per q-head against Nk keys, no causal mask.
-// The keys are cut into `splits` ranges of `kps` keys (a multiple of 128); the first kernel
-// writes each range's normalised partial output and natural-log LSE into the workspace, the
-// second merges them.
+// Each sequence's key_lens[b] keys are cut into `splits` equal ranges (whole 32-key steps); the
+// first kernel writes each range's normalised partial output and natural-log LSE into the
+// workspace, the second merges them.  `kps` is the plan's range length for Nk keys.
 struct SplitParams {
     const void* q;            // [B][Hq][Nq][d] bf16
     const void* k;            // [B][Hkv][Nk][d] bf16

@@ -75,8 +75,12 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_bf16_kernel(SplitParams p
 
     int Lk = p.Nk;
     if (p.key_lens) Lk = min(max(p.key_lens[b], 0), p.Nk);
-    const int ks = split * p.kps;
-    const int ke = min(ks + p.kps, Lk);                     // key range [ks, ke), maybe empty
+    // This sequence's Lk keys cut into p.splits ranges of equal length in whole 32-key steps
+    // (not Nk's: no workgroup is left with keys past the key length only); the last ranges may
+    // be shorter or empty.
+    const int kpr = ((Lk + p.splits - 1) / p.splits + kBC - 1) / kBC * kBC;
+    const int ks = split * kpr;
+    const int ke = min(ks + kpr, Lk);                       // key range [ks, ke), maybe empty
     const int nsteps = ke > ks ? (ke - ks + kBC - 1) / kBC : 0;
 
     // This lane's row: (q-head g of the group, query qi); rows >= R are padding.
@@ -253,41 +257,70 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_bf16_kernel(SplitParams p
     }
 }
 
-// Merge of the key ranges' partial results: one workgroup per query row; thread t takes 8
-// columns (chunk t % (D/8)) of the ranges t / (D/8), t / (D/8) + SP, ...; the partial sums are
-// reduced through LDS.
+// Merge of the key ranges' partial results (the tutorial's step-3 identity over ranges): one
+// workgroup per query row; thread t takes 8 columns (chunk t % (D/8)) of the ranges t / (D/8),
+// t / (D/8) + SP, ...  It folds them into a running (max m, weight sum l, weighted output) with
+// the loads of NI ranges issued before any is used, so a row costs one memory round trip for up
+// to NI * SP ranges; the threads' partial merges then meet in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitParams p) {
     constexpr int CH = D / 8;          // 8-column chunks per row
     constexpr int SP = 256 / CH;       // ranges taken in parallel
-    __shared__ float red_m[256];
+    constexpr int NI = 4;              // ranges per thread per round trip
+    __shared__ float red_m[SP];
     __shared__ float red_l[SP];
     __shared__ f32x4 red_o[SP][CH][2];
     const long long rows = (long long)p.B * p.Hq * p.Nq;
     const long long row = blockIdx.x;
     const int t = threadIdx.x, ch = t % CH, s0 = t / CH;
 
-    float M = kNegInf;
-    for (int s = s0; s < p.splits; s += SP) M = fmaxf(M, p.lpart[s * rows + row]);
-    red_m[t] = M;
-    __syncthreads();
-    M = kNegInf;
-    for (int i = 0; i < 256; i += CH) M = fmaxf(M, red_m[i]);   // one entry per range group
-
+    // Every thread with this s0 folds the same ranges (other columns), so m and l agree among them.
+    float m = kNegInf, l = 0.f;
     f32x4 a = {0.f, 0.f, 0.f, 0.f}, bq = {0.f, 0.f, 0.f, 0.f};
-    float L = 0.f;
-    if (M != kNegInf) {
-        for (int s = s0; s < p.splits; s += SP) {
-            const float wgt = exp2_hw((p.lpart[s * rows + row] - M) * kLog2e);   // 0 for -inf
-            L += wgt;
-            const f32x4* src = reinterpret_cast<const f32x4*>(p.opart + (s * rows + row) * D + 8 * ch);
-            a += wgt * src[0];
-            bq += wgt * src[1];
+    for (int sb = s0; sb < p.splits; sb += NI * SP) {
+        float lp[NI];
+        f32x4 oa[NI], ob[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int s = sb + i * SP;
+            lp[i] = kNegInf;
+            oa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            ob[i] = oa[i];
+            if (s < p.splits) {
+                lp[i] = p.lpart[s * rows + row];
+                const f32x4* src =
+                    reinterpret_cast<const f32x4*>(p.opart + (s * rows + row) * D + 8 * ch);
+                oa[i] = src[0];
+                ob[i] = src[1];
+            }
+        }
+        float mn = m;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) mn = fmaxf(mn, lp[i]);
+        if (mn != kNegInf) {
+            const float r = exp2_hw((m - mn) * kLog2e);   // 0 while m is -inf (l, a are 0 then)
+            l *= r;
+            a *= r;
+            bq *= r;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const float wgt = exp2_hw((lp[i] - mn) * kLog2e);   // 0 for an empty range
+                l += wgt;
+                a += wgt * oa[i];
+                bq += wgt * ob[i];
+            }
+            m = mn;
         }
     }
-    red_o[s0][ch][0] = a;
-    red_o[s0][ch][1] = bq;
-    if (ch == 0) red_l[s0] = L;
+    if (ch == 0) red_m[s0] = m;
+    __syncthreads();
+    float M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < SP; ++i) M = fmaxf(M, red_m[i]);
+    const float wt = m == kNegInf ? 0.f : exp2_hw((m - M) * kLog2e);
+    red_o[s0][ch][0] = wt * a;
+    red_o[s0][ch][1] = wt * bq;
+    if (ch == 0) red_l[s0] = wt * l;
     __syncthreads();
     if (t < CH) {
         f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = {0.f, 0.f, 0.f, 0.f};
