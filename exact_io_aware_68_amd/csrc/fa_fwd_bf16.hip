@@ -217,8 +217,9 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
     // and partial sum far from the fp32 and bf16 limits.  The common step computes no row max.
     auto exponentiate = [&](int j, const f32x16 (&st)[NH][kNT], bf16x8 (&pf)[NH][kNT][2]) {
         // Window instances: a row may see no key in the workgroup's first steps, so its
-        // reference point starts unset (-inf) and, until every row of the wave has met its first
-        // visible key (steps up to jfresh), each step moves it to the row max so far.  A
+        // reference point starts unset (-inf); until every row of the wave has met its first
+        // visible key (steps up to jfresh), each step sets the point of a row that has none yet
+        // to the row max of the step (no rescale: such a row's O and l are still zero).  A
         // placeholder point would let exponentials of very negative scores underflow to zero.
         const bool fresh = WIN && j <= jfresh;
 #pragma unroll
@@ -236,12 +237,17 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
                         rs += pe[t][r];
                     }
             };
-            bool move = fresh;
-            if (!fresh) {
-                expo();
-                move = __builtin_amdgcn_ballot_w64(!(rs <= kSumCap)) != 0;
+            if (fresh) {
+                float mx = kNegInf;
+#pragma unroll
+                for (int t = 0; t < kNT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[h][t][r]);
+                mx = max_with_partner(mx) * C;
+                if (m[h] == kNegInf) m[h] = mx;   // still -inf for a row that sees no key yet
             }
-            if (move) {
+            expo();
+            if (__builtin_amdgcn_ballot_w64(!(rs <= kSumCap)) != 0) {
                 float mx = kNegInf;
 #pragma unroll
                 for (int t = 0; t < kNT; ++t)
