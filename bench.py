@@ -270,6 +270,183 @@ bench.py compares with the kernel's current sources: a stale row reads as unmeas
     print(txt)
 
 
+# MI355X (gfx950): 8 XCDs x 4 shader engines, 256 CUs, 4 SIMDs per CU.
+N_SE, N_CU, N_SIMD = 32, 256, 1024
+
+
+def _kernel_key(name):
+    key = next((k for frag, k in KERNEL_MATCH if frag in name), None)
+    if key is None and "copyBuffer" in name:
+        key = "copy"
+    return key
+
+
+def _trace_durations(path):
+    """{dispatch id: (kernel key, duration ns, start ns)} from a rocprofv3 kernel_trace.csv."""
+    import csv
+    out = {}
+    for r in csv.DictReader(open(path)):
+        key = _kernel_key(r["Kernel_Name"])
+        if key is not None:
+            s0, s1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            out[r["Dispatch_Id"]] = (key, s1 - s0, s0)
+    return out
+
+
+def _dispatch_counters(path):
+    """{dispatch id: (kernel key, {counter: value})} from a rocprofv3 counter_collection.csv
+    (values of one counter within a dispatch summed)."""
+    import csv
+    out = {}
+    for r in csv.DictReader(open(path)):
+        key = _kernel_key(r["Kernel_Name"])
+        if key is None:
+            continue
+        _, c = out.setdefault(r["Dispatch_Id"], (key, {}))
+        c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def trace_summary(d, workload, steps, cmd_note):
+    """Write profiles/kernels_<workload>.md from a rocprofv3 --kernel-trace run in directory d
+    (run_kernel_trace.csv): per kernel the calls, average, min and max duration over every
+    dispatch and the average over the last `steps` (the bench's timed steps), next to the
+    HIP-event averages the traced bench printed (d/bench.json, if present)."""
+    import statistics
+    tr = sorted(_trace_durations(os.path.join(d, "run_kernel_trace.csv")).values(),
+                key=lambda t: t[2])
+    by = {}
+    for key, dur, _ in tr:
+        by.setdefault(key, []).append(dur / 1e3)
+    live = None
+    try:
+        live = json.loads(open(os.path.join(d, "bench.json")).read().strip().splitlines()[-1])
+    except (OSError, ValueError, IndexError):
+        pass
+    rows = []
+    for key, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        last = v[-steps:]
+        rows.append(f"| {key} | {len(v)} | {statistics.mean(v):.1f} | {min(v):.1f} | {max(v):.1f} "
+                    f"| {statistics.mean(last):.1f} |")
+    live_txt = ""
+    if live:
+        km = live.get("kernels_ms") or {}
+        live_txt = ("\nLive HIP-event averages printed by the traced bench (timed steps): " +
+                    ", ".join(f"{k} {v * 1e3:.1f} µs" for k, v in km.items()) + ".\n")
+        if live.get("roofline"):
+            r = live["roofline"]
+            live_txt += (f"Its roofline line: kernel {r.get('kernel')}, achieved {r.get('achieved')} "
+                         f"{r.get('unit')} of {r.get('peak')} (frac {r.get('frac')}).\n")
+    txt = f"""# Kernel durations — workload {workload}
+
+Command (from the repository root on the MI355X box; $REPO is the repository):
+
+{cmd_note}
+
+`run_kernel_trace.csv`, every dispatch of each kernel, and the average over the last {steps}
+dispatches (the bench's timed steps; the warm-up dispatches come first):
+
+| Kernel | Calls | Average, all (µs) | Min (µs) | Max (µs) | Average, last {steps} (µs) |
+|---|---|---|---|---|---|
+""" + "\n".join(rows) + "\n" + live_txt
+    open(os.path.join(ROOT, "profiles", f"kernels_{workload}.md"), "w").write(txt)
+    print(txt)
+
+
+SQ_PASSES = {   # rocprofv3 --pmc passes of at most 8 SQ counters (and GRBM in the last)
+    "p1": "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS "
+          "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_TRANS_F32",
+    "p2": "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_ANY SQ_WAIT_INST_LDS SQ_WAIT_ANY "
+          "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_VMEM SQ_WAIT_INST_ANY",
+    "p3": "SQ_LDS_DATA_FIFO_FULL SQ_LDS_ADDR_CONFLICT SQ_INSTS_SALU SQ_INSTS_VMEM_RD "
+          "SQ_INSTS_VMEM_WR SQ_VALU_MFMA_COEXEC_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_BRANCH",
+    "p4": "SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS_LOAD_BANDWIDTH GRBM_GUI_ACTIVE",
+}
+
+
+def sq_summary(d, workload, cmd_note):
+    """Write profiles/sq_counters_<workload>.md from the four --pmc passes (with --kernel-trace) in
+    directory d: per kernel the mean of each counter over its dispatches, and derived rates.  The
+    shader clock of a dispatch is SQ_BUSY_CYCLES / N_SE over the dispatch's own duration."""
+    import statistics
+    counters, dur = {}, {}
+    for ps in SQ_PASSES:
+        c = _dispatch_counters(os.path.join(d, f"{ps}_counter_collection.csv"))
+        t = _trace_durations(os.path.join(d, f"{ps}_kernel_trace.csv"))
+        for did, (key, vals) in c.items():
+            for name, v in vals.items():
+                counters.setdefault(key, {}).setdefault(name, []).append(v)
+            if ps == "p1" and did in t and "SQ_BUSY_CYCLES" in vals:
+                dur.setdefault(key, []).append((t[did][1], vals["SQ_BUSY_CYCLES"]))
+            if ps == "p4" and did in t and "GRBM_GUI_ACTIVE" in vals:
+                dur.setdefault(key + "#grbm", []).append((t[did][1], vals["GRBM_GUI_ACTIVE"]))
+    kernels = [k for k in ("fwd_bf16", "bwd_prep", "bwd_dkdv", "bwd_dq", "fwd_window", "fwd_sparse",
+                           "splitkv", "splitkv_merge") if k in counters]
+    names = [n for ps in SQ_PASSES.values() for n in ps.split()]
+    mean = {k: {n: statistics.mean(counters[k][n]) for n in names if n in counters[k]}
+            for k in kernels}
+    lines = ["| Counter | " + " | ".join(kernels) + " |", "|---" * (len(kernels) + 1) + "|"]
+    for n in names:
+        lines.append(f"| {n} | " + " | ".join(f"{mean[k][n]:,.0f}" if n in mean[k] else "-"
+                                             for k in kernels) + " |")
+
+    def derived(k):
+        m = mean[k]
+        cyc = m.get("SQ_BUSY_CYCLES", 0.0) / N_SE          # cycles of the dispatch per engine
+        mf = m.get("SQ_INSTS_MFMA", 0.0)
+        ghz = [b / N_SE / ns for ns, b in dur.get(k, []) if ns > 0]
+        grbm = [g / 8 / ns for ns, g in dur.get(k + "#grbm", []) if ns > 0]
+        wc = m.get("SQ_WAVE_CYCLES", 0.0) or 1.0
+        out = {
+            "duration (µs, counter run)": statistics.mean(ns for ns, _ in dur[k]) / 1e3 if dur.get(k) else None,
+            "shader clock, SQ_BUSY_CYCLES / 32 per duration (GHz)": statistics.mean(ghz) if ghz else None,
+            "GRBM_GUI_ACTIVE / 8 per duration (GHz)": statistics.mean(grbm) if grbm else None,
+            "MFMA busy (of SIMD-cycles)": m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * N_SIMD) if cyc else None,
+            "MFMA and VALU co-executing (of MFMA busy)":
+                m.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / m["SQ_VALU_MFMA_BUSY_CYCLES"]
+                if m.get("SQ_VALU_MFMA_BUSY_CYCLES") else None,
+            "VALU instructions per MFMA (excl. MFMA)": (m.get("SQ_INSTS_VALU", 0.0) - mf) / mf if mf else None,
+            "LDS instructions per MFMA": m.get("SQ_INSTS_LDS", 0.0) / mf if mf else None,
+            "LDS busy (SQ_LDS_IDX_ACTIVE / CU-cycles)": m.get("SQ_LDS_IDX_ACTIVE", 0.0) / (cyc * N_CU) if cyc else None,
+            "wave time executing": m.get("SQ_ACTIVE_INST_ANY", 0.0) / wc,
+            "wave time waiting": m.get("SQ_WAIT_ANY", 0.0) / wc,
+            "wave time waiting to issue": m.get("SQ_WAIT_INST_ANY", 0.0) / wc,
+        }
+        return out
+
+    der = {k: derived(k) for k in kernels}
+    dl = ["| Metric | " + " | ".join(kernels) + " |", "|---" * (len(kernels) + 1) + "|"]
+    for name in der[kernels[0]]:
+        cells = []
+        for k in kernels:
+            v = der[k][name]
+            if v is None:
+                cells.append("-")
+            elif "GHz" in name or "per MFMA" in name:
+                cells.append(f"{v:.2f}")
+            elif "µs" in name:
+                cells.append(f"{v:.1f}")
+            else:
+                cells.append(f"{100 * v:.1f} %")
+        dl.append(f"| {name} | " + " | ".join(cells) + " |")
+    txt = f"""# Instruction and stall counters — workload {workload}
+
+Four `rocprofv3 --pmc` passes (each with `--kernel-trace`, so that every dispatch's counters sit
+beside its own duration), one counter group each, means over each kernel's dispatches; run from
+/tmp with TMPDIR=/tmp ($REPO is the repository):
+
+{cmd_note}
+
+Counters: SQ_INSTS_VALU includes the MFMAs; ACTIVE / WAIT / WAVE cycle counters are summed over
+waves; SQ_BUSY_CYCLES is summed over the {N_SE} shader engines, SQ_VALU_MFMA_BUSY_CYCLES over
+the {N_SIMD} SIMDs and SQ_LDS_IDX_ACTIVE over the {N_CU} CUs.  One v_mfma_f32_32x32x16_bf16 keeps
+a SIMD's matrix unit busy for 32 cycles.
+
+""" + "\n".join(lines) + "\n\nDerived, per kernel:\n\n" + "\n".join(dl) + "\n"
+    open(os.path.join(ROOT, "profiles", f"sq_counters_{workload}.md"), "w").write(txt)
+    print(txt)
+
+
 def cpu_baseline(x, w, budget_s=20.0):
     """Time the fp64 oracle (as written, untuned) forward + backward on whole heads of the same
     workload, as many as fit the time budget (at least one)."""
@@ -656,14 +833,42 @@ def main():
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--traffic-summary", metavar="DIR",
                     help="write profiles/hbm_traffic_<workload>.md from rocprofv3 --pmc CSVs")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="write profiles/kernels_<workload>.md from a rocprofv3 kernel trace")
+    ap.add_argument("--sq-summary", metavar="DIR",
+                    help="write profiles/sq_counters_<workload>.md from rocprofv3 --pmc passes")
     args = ap.parse_args()
     if args.traffic_summary:
         cmd = TRAFFIC_CMD
         if args.workload != "c3":
-            cmd = (cmd.replace("bench.py --steps", f"bench.py --workload {args.workload} --steps")
-                      .replace("--traffic-summary", f"--workload {args.workload} --traffic-summary")
-                      .replace("$OUT/pmc", "$OUT/pmcd"))
+            W = args.workload
+            cmd = (f"    cd /tmp && export TMPDIR=/tmp\n"
+                   f"    for C in FETCH_SIZE WRITE_SIZE; do\n"
+                   f"      rocprofv3 --pmc $C -T -f csv -d $OUT/pmcd_{W} -o bench_$C -- \\\n"
+                   f"          python3 $REPO/bench.py --workload {W} --steps 2 --warmup 1 --no-cpu-baseline\n"
+                   f"    done\n"
+                   f"    cp $OUT/pmc/copy_* $OUT/pmcd_{W}/   # the copy calibration runs of the c3 summary\n"
+                   f"    python3 $REPO/bench.py --workload {W} --traffic-summary $OUT/pmcd_{W}")
         traffic_summary(args.traffic_summary, args.workload, cmd)
+        return
+    if args.trace_summary:
+        wl = "" if args.workload == "c3" else f" --workload {args.workload}"
+        cmd = (f"    cd /tmp && export TMPDIR=/tmp\n"
+               f"    rocprofv3 --kernel-trace --stats -T -f csv -d $OUT/trace_{args.workload} -o run -- \\\n"
+               f"        python3 $REPO/bench.py{wl} --steps {args.steps} --warmup {args.warmup} "
+               f"--no-cpu-baseline --cold-steps 0 --no-other-configs > $OUT/trace_{args.workload}/bench.json\n"
+               f"    python3 $REPO/bench.py{wl} --steps {args.steps} --warmup {args.warmup} "
+               f"--trace-summary $OUT/trace_{args.workload}")
+        trace_summary(args.trace_summary, args.workload, args.steps, cmd)
+        return
+    if args.sq_summary:
+        wl = "" if args.workload == "c3" else f" --workload {args.workload}"
+        cmd = "\n".join(
+            f"    timeout -s KILL 60 rocprofv3 --pmc {c} --kernel-trace -T -f csv -d $OUT/sq_{args.workload} "
+            f"-o {ps} -- \\\n        python3 $REPO/bench.py{wl} --steps 2 --warmup 1 --no-cpu-baseline "
+            f"--cold-steps 0 --no-other-configs" for ps, c in SQ_PASSES.items())
+        cmd += f"\n    python3 $REPO/bench.py{wl} --sq-summary $OUT/sq_{args.workload}"
+        sq_summary(args.sq_summary, args.workload, cmd)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the attention path is "
