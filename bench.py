@@ -853,10 +853,11 @@ def main():
         return
     if args.trace_summary:
         wl = "" if args.workload == "c3" else f" --workload {args.workload}"
+        extra = " --cold-steps 0 --no-other-configs" if args.workload in ("c1", "c2", "c3", "c4", "c5") else ""
         cmd = (f"    cd /tmp && export TMPDIR=/tmp\n"
                f"    rocprofv3 --kernel-trace --stats -T -f csv -d $OUT/trace_{args.workload} -o run -- \\\n"
                f"        python3 $REPO/bench.py{wl} --steps {args.steps} --warmup {args.warmup} "
-               f"--no-cpu-baseline --cold-steps 0 --no-other-configs > $OUT/trace_{args.workload}/bench.json\n"
+               f"--no-cpu-baseline{extra} > $OUT/trace_{args.workload}/bench.json\n"
                f"    python3 $REPO/bench.py{wl} --steps {args.steps} --warmup {args.warmup} "
                f"--trace-summary $OUT/trace_{args.workload}")
         trace_summary(args.trace_summary, args.workload, args.steps, cmd)
