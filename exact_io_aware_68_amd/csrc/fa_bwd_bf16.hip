@@ -233,65 +233,89 @@ __global__ __launch_bounds__(kThreadsKV) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) pa[4 * g + e] = d4[e];
             }
-            // The S chain, then the dP chain (each MFMA accumulates onto the previous one's
-            // result; the other wave on the SIMD fills the gaps).
+            // Three chains of MFMAs, each accumulating onto the previous one's result, with the
+            // VALU work placed beside the chain it does not depend on:
+            //   S chain;
+            //   dP chain  beside  P = 2^(S C - LSE2) (needs S only);
+            //   dV chain  beside  -dS = P (D - dP) (needs dP) and its bf16 operand;
+            //   dK chain.
+            // The causal mask hides score r when the key lies past its row: rel > 8(r/4) + r%4
+            // with rel fixed per lane (and pushed past every row for keys at or beyond the key
+            // length).  Operands are read one MFMA ahead; each fence fixes the order.
             auto rds = [&](int s, bf16x8 (&x)[2]) {
                 const int k = s % NS;
                 x[0] = __builtin_bit_cast(bf16x8, ld16((s < NS ? Qc : Oc) + ro[k]));
                 x[1] = __builtin_bit_cast(bf16x8, ld16((s < NS ? Kw : Vw) + ro[k]));
             };
+            int rel = 0;
+            if constexpr (need_mask) rel = key >= Lk ? 1 << 30 : key - i0 - 32 * hq - 4 * hh;
             bf16x8 op[2][2];
             rds(0, op[0]);
 #pragma unroll
-            for (int s = 0; s < 2 * NS; ++s) {
-                if (s + 1 < 2 * NS) rds(s + 1, op[(s + 1) & 1]);
-                if (s < NS) sa = mfma32(op[s & 1][0], op[s & 1][1], sa);
-                else pa = mfma32(op[s & 1][0], op[s & 1][1], pa);
+            for (int s = 0; s < NS; ++s) {
+                rds(s + 1, op[(s + 1) & 1]);
+                sa = mfma32(op[s & 1][0], op[s & 1][1], sa);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // P = 2^(S C - LSE2) and -dS = P (D - dP); the causal mask hides score r when the
-            // key lies past its row: rel > 8(r/4) + r%4 with rel fixed per lane (and pushed past
-            // every row for keys at or beyond the key length).
-            f32x4 l4[4];
+            constexpr int RP = 16 / NS;   // scores exponentiated per dP MFMA
+            bf16x8 pf[2], sf[2];          // B operands of dV, dK: query rows 16u + ...
+            f32x4 l4;
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                l4[g] = *reinterpret_cast<const f32x4*>(&sm.l2[cur][32 * hq + 8 * g + 4 * hh]);
-            int rel = 0;
-            if constexpr (need_mask) rel = key >= Lk ? 1 << 30 : key - i0 - 32 * hq - 4 * hh;
+            for (int s = NS; s < 2 * NS; ++s) {
+                if (s + 1 < 2 * NS) rds(s + 1, op[(s + 1) & 1]);
+                pa = mfma32(op[s & 1][0], op[s & 1][1], pa);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float pv = exp2_hw(__builtin_fmaf(sa[r], Cs, -l4[r >> 2][r & 3]));
-                if constexpr (need_mask) {
-                    const bool hide = CAUSAL ? rel > 8 * (r >> 2) + (r & 3) : key >= Lk;
-                    pv = hide ? 0.f : pv;
+                for (int x = 0; x < RP; ++x) {
+                    const int r = RP * (s - NS) + x;
+                    if ((r & 3) == 0)
+                        l4 = *reinterpret_cast<const f32x4*>(&sm.l2[cur][32 * hq + 8 * (r >> 2) + 4 * hh]);
+                    float pv = exp2_hw(__builtin_fmaf(sa[r], Cs, -l4[r & 3]));
+                    if constexpr (need_mask) {
+                        const bool hide = CAUSAL ? rel > 8 * (r >> 2) + (r & 3) : key >= Lk;
+                        pv = hide ? 0.f : pv;
+                    }
+                    sa[r] = pv;
                 }
-                sa[r] = pv;
-                pa[r] = pv * pa[r];
+                __builtin_amdgcn_sched_barrier(0);
             }
-            bf16x8 pf[2], sf[2];   // B operands of dV, dK: query rows 16u + ...
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int o8 = 8 * u;
-                pf[u] = to_bf16x8(sa[o8], sa[o8 + 1], sa[o8 + 2], sa[o8 + 3], sa[o8 + 4], sa[o8 + 5],
-                                  sa[o8 + 6], sa[o8 + 7]);
-                sf[u] = to_bf16x8(pa[o8], pa[o8 + 1], pa[o8 + 2], pa[o8 + 3], pa[o8 + 4], pa[o8 + 5],
-                                  pa[o8 + 6], pa[o8 + 7]);
-            }
+            for (int u = 0; u < 2; ++u)
+                pf[u] = to_bf16x8(sa[8 * u], sa[8 * u + 1], sa[8 * u + 2], sa[8 * u + 3],
+                                  sa[8 * u + 4], sa[8 * u + 5], sa[8 * u + 6], sa[8 * u + 7]);
             // dV^T += dO^T P, dK^T += Q^T (-dS): A = one d-column over 8 query rows (transpose
-            // reads), read one step ahead.
-            auto rdt = [&](int g, bf16x8 (&x)[2]) {
-                const int dt = g >> 1, ru = 16 * (g & 1) * D;
-                x[0] = trop(Oc + ru, tro[dt][0], tro[dt][1]);
-                x[1] = trop(Qc + ru, tro[dt][0], tro[dt][1]);
+            // reads).
+            constexpr int kRing = 3;
+            auto rdt = [&](int g, const bf16* base) {
+                return trop(base + 16 * (g & 1) * D, tro[g >> 1][0], tro[g >> 1][1]);
             };
-            bf16x8 ot[2][2];
-            rdt(0, ot[0]);
+            constexpr int RS = 16 / (2 * ND);   // scores of -dS per dV MFMA
+            // The 4 ND transposed operands (dO^T for the dV chain, then Q^T for the dK chain)
+            // pass through a ring of kRing registers, each read kRing - 1 MFMAs ahead.
+            auto rdi = [&](int i) { return rdt(i % (2 * ND), i < 2 * ND ? Oc : Qc); };
+            bf16x8 ot[kRing];
+#pragma unroll
+            for (int i = 0; i < kRing - 1; ++i) ot[i] = rdi(i);
 #pragma unroll
             for (int g = 0; g < 2 * ND; ++g) {
-                if (g + 1 < 2 * ND) rdt(g + 1, ot[(g + 1) & 1]);
-                const int dt = g >> 1, u = g & 1;
-                dva[dt] = mfma32(ot[g & 1][0], pf[u], dva[dt]);
-                dka[dt] = mfma32(ot[g & 1][1], sf[u], dka[dt]);
+                if (g + kRing - 1 < 4 * ND) ot[(g + kRing - 1) % kRing] = rdi(g + kRing - 1);
+                dva[g >> 1] = mfma32(ot[g % kRing], pf[g & 1], dva[g >> 1]);
+#pragma unroll
+                for (int x = 0; x < RS; ++x) {
+                    const int r = RS * g + x;
+                    pa[r] = sa[r] * pa[r];
+                    if ((r & 7) == 7) {
+                        const int o8 = r - 7;
+                        sf[r >> 3] = to_bf16x8(pa[o8], pa[o8 + 1], pa[o8 + 2], pa[o8 + 3],
+                                               pa[o8 + 4], pa[o8 + 5], pa[o8 + 6], pa[o8 + 7]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int g = 0; g < 2 * ND; ++g) {
+                const int i = 2 * ND + g;
+                if (i + kRing - 1 < 4 * ND) ot[(i + kRing - 1) % kRing] = rdi(i + kRing - 1);
+                dka[g >> 1] = mfma32(ot[i % kRing], sf[g & 1], dka[g >> 1]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             wait_vmem();       // this wave's share of tile it+1 has landed

@@ -141,60 +141,79 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
 
     // One 32-key compute step on the half tile at Ks / Vs holding keys k0 ..; MASK: some key of
     // the step may lie past this wave's rows or past the key length.
+    //   S^T chain (= K Q^T, rows = the 32 keys, columns = the wave's queries);
+    //   dP^T chain (= V dO^T, started from D)  beside  P = 2^(S C - LSE2) (needs S only);
+    //   -dS = P (D - dP) of keys 0..15, then the dQ^T chain over those keys  beside  -dS of
+    //   keys 16..31, then the chain over keys 16..31.
+    // Each chain accumulates onto the previous MFMA's result; its operands pass through a ring
+    // of kRing registers, each read kRing - 1 MFMAs ahead, and one fence per MFMA fixes the
+    // order.
     auto step = [&](auto mm, const bf16* Ks, const bf16* Vs, int k0) {
         constexpr bool MASK = decltype(mm)::value;
-        // S^T = K Q^T, dP^T = V dO^T: rows = the 32 keys, columns = the wave's queries.
-        // Operands of reduction step s+1 are read while the MFMAs of step s run (one fence per
-        // step keeps each read from sinking next to its MFMA).
+        constexpr int kRing = 3;
         f32x16 st = f32x16{}, pt = dvec;
-        bf16x8 ck, cv;
-        auto rd = [&](int s, bf16x8& k_, bf16x8& v_) {
-            k_ = __builtin_bit_cast(bf16x8, ld16(Ks + kro[s]));
-            v_ = __builtin_bit_cast(bf16x8, ld16(Vs + kro[s]));
+        // Row reads: i < NS the K rows of step i, then the V rows.
+        auto rd = [&](int i) {
+            return __builtin_bit_cast(bf16x8, ld16((i < NS ? Ks : Vs) + kro[i % NS]));
         };
-        rd(0, ck, cv);
+        bf16x8 rr[kRing];
+#pragma unroll
+        for (int i = 0; i < kRing - 1; ++i) rr[i] = rd(i);
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            bf16x8 nk, nv;
-            if (s + 1 < NS) rd(s + 1, nk, nv);
-            st = mfma32(ck, qf[s], st);
-            pt = mfma32(cv, of[s], pt);
+            rr[(s + kRing - 1) % kRing] = rd(s + kRing - 1);
+            st = mfma32(rr[s % kRing], qf[s], st);
             __builtin_amdgcn_sched_barrier(0);
-            if (s + 1 < NS) {
-                ck = nk;
-                cv = nv;
-            }
         }
-        // P and dS (scale applied once at the end); C row r -> key k0 + 4hh + kr(r) with
-        // kr(r) = 8(r/4) + r%4.  The key is hidden when it lies past the row or the key length,
-        // i.e. when kr(r) > thr for one lane constant thr.
+        // C row r -> key k0 + 4hh + kr(r) with kr(r) = 8(r/4) + r%4.  The key is hidden when
+        // it lies past the row or the key length, i.e. when kr(r) > thr for one lane constant
+        // thr.
         int thr = Lk - 1 - k0 - 4 * hh;
         if (CAUSAL) thr = min(thr, qrow - k0 - 4 * hh);
+        constexpr int RP = 16 / NS;   // scores exponentiated per dP MFMA
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float pv = exp2_hw(__builtin_fmaf(st[r], Cs, -lse2));
-            if constexpr (MASK) pv = 8 * (r >> 2) + (r & 3) > thr ? 0.f : pv;
-            pt[r] = pv * pt[r];   // -dS
+        for (int s = 0; s < NS; ++s) {
+            const int i = NS + s;
+            if (i + kRing - 1 < 2 * NS) rr[(i + kRing - 1) % kRing] = rd(i + kRing - 1);
+            pt = mfma32(rr[i % kRing], of[s], pt);
+#pragma unroll
+            for (int x = 0; x < RP; ++x) {
+                const int r = RP * s + x;
+                float pv = exp2_hw(__builtin_fmaf(st[r], Cs, -lse2));
+                if constexpr (MASK) pv = 8 * (r >> 2) + (r & 3) > thr ? 0.f : pv;
+                st[r] = pv;
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // dQ^T += K^T dS^T; A operand = K^T rows (d = 32 dt + c) over keys 16u + slot order,
+        // taken u-major (g = u ND + dt).
+        auto rdk = [&](int g) {
+            const int u = g / ND, dt = g % ND;
+            const bf16* base = Ks + 16 * u * D;
+            return join(lds_tr(base + tro[dt][0]), lds_tr(base + tro[dt][1]));
+        };
+        bf16x8 kr[kRing];
+#pragma unroll
+        for (int g = 0; g < kRing - 1; ++g) kr[g] = rdk(g);
         bf16x8 sf[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-            sf[u] = to_bf16x8(pt[8 * u], pt[8 * u + 1], pt[8 * u + 2], pt[8 * u + 3], pt[8 * u + 4],
-                              pt[8 * u + 5], pt[8 * u + 6], pt[8 * u + 7]);
-        __builtin_amdgcn_sched_barrier(0);
-        // dQ^T += K^T dS^T; A operand = K^T rows (d = 32 dt + c), keys 16u + slot order.
-        auto rdk = [&](int g) {
-            const bf16* base = Ks + 16 * (g & 1) * D;
-            return join(lds_tr(base + tro[g >> 1][0]), lds_tr(base + tro[g >> 1][1]));
-        };
-        bf16x8 kc = rdk(0);
+        for (int r = 0; r < 8; ++r) pt[r] = st[r] * pt[r];   // -dS, keys 0..15
+        sf[0] = to_bf16x8(pt[0], pt[1], pt[2], pt[3], pt[4], pt[5], pt[6], pt[7]);
+        constexpr int RS = 8 / ND;   // scores of -dS (keys 16..31) per MFMA over keys 0..15
 #pragma unroll
         for (int g = 0; g < 2 * ND; ++g) {
-            bf16x8 kn;
-            if (g + 1 < 2 * ND) kn = rdk(g + 1);
-            acc[g >> 1] = mfma32(kc, sf[g & 1], acc[g >> 1]);
+            if (g + kRing - 1 < 2 * ND) kr[(g + kRing - 1) % kRing] = rdk(g + kRing - 1);
+            acc[g % ND] = mfma32(kr[g % kRing], sf[g / ND], acc[g % ND]);
+            if (g < ND) {
+#pragma unroll
+                for (int x = 0; x < RS; ++x) {
+                    const int r = 8 + RS * g + x;
+                    pt[r] = st[r] * pt[r];
+                }
+                if (g == ND - 1)
+                    sf[1] = to_bf16x8(pt[8], pt[9], pt[10], pt[11], pt[12], pt[13], pt[14], pt[15]);
+            }
             __builtin_amdgcn_sched_barrier(0);
-            if (g + 1 < 2 * ND) kc = kn;
         }
     };
 
