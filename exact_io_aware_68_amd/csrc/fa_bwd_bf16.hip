@@ -203,9 +203,16 @@ __global__ __launch_bounds__(kThreadsKV) void bwd_dkdv_kernel(BwdParams p) {
         __syncthreads();
 
         // Per-lane LDS offsets.  Row reads (Q / dO rows and K / V rows c, chunk 2s + hh):
-        int ro[NS];
+        // Byte offsets of this lane's row reads (row c, chunk 2s + hh) from the start of a Q /
+        // dO tile (this wave's query half included) and of the K / V rows (this wave's keys
+        // included): each read is then one of these plus a buffer address known at compile
+        // time, which goes into the instruction's offset field.
+        int roq[NS], rok[NS];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) ro[s] = swz_at<D>(c, 16 * s + 8 * hh);
+        for (int s = 0; s < NS; ++s) {
+            roq[s] = 2 * (32 * hq * D + swz_at<D>(c, 16 * s + 8 * hh));
+            rok[s] = 2 * (32 * kg * D + swz_at<D>(c, 16 * s + 8 * hh));
+        }
         // transpose reads of dO^T / Q^T (columns 32 dt): rows 16u + ...
         int tro[ND][2];
 #pragma unroll
@@ -244,8 +251,8 @@ __global__ __launch_bounds__(kThreadsKV) void bwd_dkdv_kernel(BwdParams p) {
             // length).  Operands are read one MFMA ahead; each fence fixes the order.
             auto rds = [&](int s, bf16x8 (&x)[2]) {
                 const int k = s % NS;
-                x[0] = __builtin_bit_cast(bf16x8, ld16((s < NS ? Qc : Oc) + ro[k]));
-                x[1] = __builtin_bit_cast(bf16x8, ld16((s < NS ? Kw : Vw) + ro[k]));
+                x[0] = __builtin_bit_cast(bf16x8, ld16((const char*)(s < NS ? sm.q[cur] : sm.o[cur]) + roq[k]));
+                x[1] = __builtin_bit_cast(bf16x8, ld16((const char*)(s < NS ? sm.k : sm.v) + rok[k]));
             };
             int rel = 0;
             if constexpr (need_mask) rel = key >= Lk ? 1 << 30 : key - i0 - 32 * hq - 4 * hh;
