@@ -140,12 +140,18 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 
-// Workgroup order.  Workgroups are handed to the 8 XCDs round-robin by id; remapping so that
-// each XCD receives a contiguous range of logical indices keeps all tiles of one head on one XCD
-// (and its L2), so the K/V re-reads of neighbouring tiles hit in that L2.
-__device__ __forceinline__ int xcd_logical_block(int bid, int nblk) {
+// Workgroup order.  Logical index = head * ntile + tile rank (rank 0 carries the most work).
+// Workgroups are handed to the 8 XCDs round-robin by id; remapping so that each XCD receives a
+// contiguous share of logical indices keeps all tiles of one head on one XCD (and its L2), so
+// the K/V re-reads of neighbouring tiles hit in that L2.  When the share is whole heads, the
+// XCD runs it rank by rank (rank 0 of each of its heads, then rank 1, ...): longest first over
+// the whole share, not head by head, which would start the long tiles of its last head late.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblk, int ntile) {
     if ((nblk & 7) != 0) return bid;
-    return (bid & 7) * (nblk >> 3) + (bid >> 3);
+    const int share = nblk >> 3, x = bid & 7, pos = bid >> 3;
+    if (share % ntile != 0) return x * share + pos;
+    const int hx = share / ntile;   // heads of this XCD
+    return x * share + (pos % hx) * ntile + pos / hx;
 }
 
 // Tiles in LDS are row-major with their 16-byte chunks XOR-swizzled per row, so that they can
