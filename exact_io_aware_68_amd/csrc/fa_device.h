@@ -143,13 +143,15 @@ __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*
 // Workgroup order.  Logical index = head * ntile + tile rank (rank 0 carries the most work).
 // Workgroups are handed to the 8 XCDs round-robin by id; remapping so that each XCD receives a
 // contiguous share of logical indices keeps all tiles of one head on one XCD (and its L2), so
-// the K/V re-reads of neighbouring tiles hit in that L2.  When the share is whole heads, the
-// XCD runs it rank by rank (rank 0 of each of its heads, then rank 1, ...): longest first over
-// the whole share, not head by head, which would start the long tiles of its last head late.
-__device__ __forceinline__ int xcd_logical_block(int bid, int nblk, int ntile) {
+// the K/V re-reads of neighbouring tiles hit in that L2.  Where the tiles' work differs
+// (ranked = true: causal) and the share is whole heads, the XCD runs it rank by rank (rank 0 of
+// each of its heads, then rank 1, ...): longest first over the whole share, not head by head,
+// which would start the long tiles of its last head late.  Equal tiles keep the head-by-head
+// order, whose concurrent workgroups share one head's K and V in the L2.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblk, int ntile, bool ranked) {
     if ((nblk & 7) != 0) return bid;
     const int share = nblk >> 3, x = bid & 7, pos = bid >> 3;
-    if (share % ntile != 0) return x * share + pos;
+    if (!ranked || share % ntile != 0) return x * share + pos;
     const int hx = share / ntile;   // heads of this XCD
     return x * share + (pos % hx) * ntile + pos / hx;
 }
