@@ -73,6 +73,14 @@ CASES = [  # (B, Hq, Hkv, N, d, causal, padded)
     (1, 2, 2, 63, 64, False, False),
     (1, 2, 1, 129, 128, True, False),
     (1, 1, 1, 640, 128, True, False),
+    # causal grids whose per-XCD share takes each branch of the workgroup order: three heads
+    # (ranked over all), one pair of heads, one head, a share that is not whole heads, and a
+    # pair of grouped-query heads
+    (1, 24, 24, 384, 128, True, False),
+    (2, 8, 8, 512, 64, True, True),
+    (1, 8, 8, 640, 128, True, False),
+    (1, 4, 4, 768, 128, True, False),
+    (1, 16, 4, 512, 128, True, True),
 ]
 
 
