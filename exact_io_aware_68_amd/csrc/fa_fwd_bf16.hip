@@ -339,6 +339,20 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
     }
     __syncthreads();   // keys 0..31 in buffer 1 are overwritten by K tile 1 during steps 0, 1
 
+    // Window instances: the steps that hold a key visible to some row of this wave (steps
+    // outside are hidden from all of its rows: their P is 0, so skipping their products changes
+    // no bit of O or l).  The wave still takes part in those steps' copies and barriers.
+    int jact_lo = 0, jact_hi = 1 << 30;
+    if constexpr (WIN) {
+        if (wl >= 0) jact_lo = max(0, (q0 - wl - kb) / kBC);
+        if (wr >= 0) jact_hi = max(q0 + kWR - 1 + wr - kb, -1) / kBC;
+        jact_hi = min(jact_hi, Lr > 0 ? (Lr - 1) / kBC : -1);
+        if (wr >= 0 && q0 + kWR - 1 + wr - kb < 0) jact_hi = -1;
+    }
+    auto active = [&](auto maskn, int jj) {   // (unmasked steps are always active)
+        if constexpr (WIN && decltype(maskn)::value) return jj >= jact_lo && jj <= jact_hi;
+        else return true;
+    };
     auto step = [&](auto maskn, auto odd, auto ph, int j, f32x16 (&cur)[NH][kNT],
                     f32x16 (&nxt)[NH][kNT]) {
         constexpr int P = decltype(ph)::value;
@@ -350,10 +364,12 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
             if (T + 1 < nkt) load_k(T + 1, tb ^ 1);
             if (T + 1 < nlt) load_v(T + 1, tb ^ 1);
         }
-        scores(sm.k[tb] + half * kBC * D, nxt);             // MFMA (= ksub(j + 1)) ...
-        exponentiate(j, cur, pf);                           // ... alongside VALU
-        if constexpr (decltype(maskn)::value) mask(j + 1, nxt);
-        pv(sm.v[tb] + half * kBC * D, pf);                  // (= vsub(j))
+        const bool act_j = active(maskn, j), act_n = active(maskn, j + 1);
+        if (act_n) scores(sm.k[tb] + half * kBC * D, nxt);  // MFMA (= ksub(j + 1)) ...
+        if (act_j) exponentiate(j, cur, pf);                // ... alongside VALU
+        if constexpr (decltype(maskn)::value)
+            if (act_n) mask(j + 1, nxt);
+        if (act_j) pv(sm.v[tb] + half * kBC * D, pf);       // (= vsub(j))
         if constexpr (decltype(odd)::value) {
             wait_vmem();       // this wave's share of tiles T+1 has landed
             __syncthreads();   // tiles T+1 visible; buffers T&1 free
@@ -408,11 +424,15 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
     }
     if (j + 1 < ntiles) {
         step(Flag<true>{}, Flag<false>{}, Phase<-1>{}, j, sa, sb);   // no loads left: none issued
-        exponentiate(j + 1, sb, pf);
-        pv(vsub(j + 1), pf);
+        if (active(Flag<true>{}, j + 1)) {
+            exponentiate(j + 1, sb, pf);
+            pv(vsub(j + 1), pf);
+        }
     } else if (j < ntiles) {
-        exponentiate(j, sa, pf);
-        pv(vsub(j), pf);
+        if (active(Flag<true>{}, j)) {
+            exponentiate(j, sa, pf);
+            pv(vsub(j), pf);
+        }
     }
 
     // ---- epilogue: O = Otilde / l (rounded to bf16), LSE = (m + log2 l) * ln 2 ---------------
