@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kThreadsKV) void bwd_dkdv_kernel(BwdParams p) {
     const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
     const int N = p.N;
     const int nkt = (N + kBK - 1) / kBK;
-    const int lin = xcd_logical_block(blockIdx.x, gridDim.x, nkt, CAUSAL);
+    const int lin = xcd_logical_block(blockIdx.x, gridDim.x, nkt, CAUSAL, 4ll * p.N * D);
     const int head = lin / nkt;                       // (b, hkv)
     const int kt = lin - head * nkt;                  // causal: low kt = most work, first
     const int b = head / p.Hkv, hkv = head - b * p.Hkv;

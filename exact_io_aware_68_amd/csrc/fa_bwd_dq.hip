@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
     const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
     const int N = p.N;
     const int nqt = (N + kBR - 1) / kBR;
-    const int lin = xcd_logical_block(blockIdx.x, gridDim.x, nqt, CAUSAL);
+    const int lin = xcd_logical_block(blockIdx.x, gridDim.x, nqt, CAUSAL, 4ll * p.N * D);
     const int head = lin / nqt;
     int qt = lin - head * nqt;
     if (CAUSAL) qt = nqt - 1 - qt;                       // longest rows first

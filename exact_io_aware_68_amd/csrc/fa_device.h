@@ -144,19 +144,21 @@ __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*
 // Workgroups are handed to the 8 XCDs round-robin by id; remapping so that each XCD receives a
 // contiguous share of logical indices keeps all tiles of one head on one XCD (and its L2), so
 // the K/V re-reads of neighbouring tiles hit in that L2.  Where the tiles' work differs
-// (ranked = true: causal) and the share is whole heads, the XCD runs its heads in pairs, each
-// pair rank by rank (rank 0 of both heads, then rank 1, ...), so long tiles start early: run
-// head by head, an XCD starts the long tiles of its last head late (about 1.5x the balanced
-// time with 32 query tiles per head).  Ranking over all of the XCD's heads at once balanced as
-// well but kept four heads' K and V live in the L2 and tripled its misses; pairs (which are
-// also grouped-query neighbours, sharing K and V) keep the misses near head-by-head.  Equal
-// tiles keep the head-by-head order.
-__device__ __forceinline__ int xcd_logical_block(int bid, int nblk, int ntile, bool ranked) {
+// (ranked = true: causal) and the share is whole heads, the XCD runs them rank by rank (rank 0
+// of each head, then rank 1, ...) so that long tiles start early: run head by head, an XCD
+// starts the long tiles of its last head late, and on a short grid (one round of workgroups)
+// a CU can receive two long tiles.  Ranking over all of the XCD's heads at once is used while
+// their K and V (head_bytes each) fit in the 4 MB L2; beyond that it multiplies the L2 misses
+// (three times at N = 8192), so the heads go in pairs (grouped-query neighbours, which share
+// K and V), each pair rank by rank.  Equal tiles keep the head-by-head order.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblk, int ntile, bool ranked,
+                                                 long long head_bytes) {
     if ((nblk & 7) != 0) return bid;
     const int share = nblk >> 3, x = bid & 7, pos = bid >> 3;
     if (!ranked || share % ntile != 0) return x * share + pos;
     const int hx = share / ntile;   // heads of this XCD
-    if ((hx & 1) != 0) return x * share + (pos % hx) * ntile + pos / hx;   // odd: rank over all
+    if ((hx & 1) != 0 || hx * head_bytes <= (4ll << 20))   // rank over all of them
+        return x * share + (pos % hx) * ntile + pos / hx;
     const int pg = pos / (2 * ntile), q2 = pos % (2 * ntile);   // pair of heads, place in it
     return x * share + (2 * pg + (q2 & 1)) * ntile + (q2 >> 1);
 }

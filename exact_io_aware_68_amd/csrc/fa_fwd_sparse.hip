@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sparse_bf16_kernel(FwdParams 
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
     const int nqt = (p.N + kBR - 1) / kBR;
-    const int lin = xcd_logical_block(blockIdx.x, gridDim.x, nqt, CAUSAL);
+    const int lin = xcd_logical_block(blockIdx.x, gridDim.x, nqt, CAUSAL, 4ll * p.N * D);
     const int head = lin / nqt;
     int qt = lin - head * nqt;
     if (CAUSAL) qt = nqt - 1 - qt;                       // longest rows first

@@ -41,7 +41,7 @@ CASES = [  # (B, Hq, Hkv, N, d, density, causal, padded)
     (2, 2, 2, 300, 64, 0.7, True, False),
     (1, 2, 2, 129, 128, 0.4, False, False),
     (1, 4, 4, 1500, 128, 0.1, True, False),
-    (2, 8, 4, 512, 128, 0.3, True, False),   # causal: each XCD runs one pair of heads
+    (2, 8, 4, 512, 128, 0.3, True, False),   # causal: each XCD ranks two heads together
 ]
 
 

@@ -55,7 +55,8 @@ CASES = [  # (B, Hq, Hkv, N, d, causal, padded)
     (1, 8, 2, 700, 128, True, True),
     (1, 4, 1, 450, 64, True, False),
     # causal grids whose per-XCD share takes each branch of the workgroup order (dK/dV and dQ):
-    # three heads, one pair, and grouped-query heads whose dK/dV share is not whole heads
+    # three heads, two heads ranked together, and grouped-query heads whose dK/dV share is not
+    # whole heads (pairs of heads: the full-size c5 test)
     (1, 24, 24, 384, 128, True, False),
     (2, 8, 8, 512, 64, True, False),
     (1, 16, 4, 512, 128, True, True),

@@ -74,8 +74,9 @@ CASES = [  # (B, Hq, Hkv, N, d, causal, padded)
     (1, 2, 1, 129, 128, True, False),
     (1, 1, 1, 640, 128, True, False),
     # causal grids whose per-XCD share takes each branch of the workgroup order: three heads
-    # (ranked over all), one pair of heads, one head, a share that is not whole heads, and a
-    # pair of grouped-query heads
+    # (ranked over all), two heads whose K and V fit in the L2 (ranked together), one head, a
+    # share that is not whole heads, and grouped-query heads; shares ranked in pairs of heads
+    # (K and V past the L2) are the full-size c3, c4 and c5 tests
     (1, 24, 24, 384, 128, True, False),
     (2, 8, 8, 512, 64, True, True),
     (1, 8, 8, 640, 128, True, False),
