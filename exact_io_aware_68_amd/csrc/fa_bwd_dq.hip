@@ -221,14 +221,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdParams p) {
     wait_vmem();
     __syncthreads();
 
-    // One 64-key tile; the buffer is a constant (CC >= 0) or t & 1.
+    // One 64-key tile; the buffer is a constant (CC >= 0) or t & 1.  In a masked tile a wave
+    // skips the steps whose keys all lie past its last row or the key length: their P is 0, so
+    // they would add nothing to dQ.  The wave still takes part in the tile's copies and barrier.
+    const int wlast = CAUSAL ? min(Lk - 1, q0 + 31) : Lk - 1;   // last key some row of the wave sees
     auto tile = [&](int t, auto cc, auto mm) {
         constexpr int CC = decltype(cc)::value;
+        constexpr bool MASK = decltype(mm)::value;
         const int cur = CC < 0 ? t & 1 : CC;
         if (t + 1 < ntiles) stage(t + 1, cur ^ 1);   // that buffer was released at the last barrier
         const int k0 = t * kLT;
-        step(mm, sm.k[cur], sm.v[cur], k0);
-        if (k0 + kBC < kend) step(mm, sm.k[cur] + kBC * D, sm.v[cur] + kBC * D, k0 + kBC);
+        if (!MASK || k0 <= wlast) step(mm, sm.k[cur], sm.v[cur], k0);
+        if (k0 + kBC < kend && (!MASK || k0 + kBC <= wlast))
+            step(mm, sm.k[cur] + kBC * D, sm.v[cur] + kBC * D, k0 + kBC);
         wait_vmem();       // this wave's share of tile t+1 has landed
         __syncthreads();   // tile t+1 visible; buffer cur free
     };

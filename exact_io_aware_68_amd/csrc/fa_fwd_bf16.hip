@@ -339,9 +339,11 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
     }
     __syncthreads();   // keys 0..31 in buffer 1 are overwritten by K tile 1 during steps 0, 1
 
-    // Window instances: the steps that hold a key visible to some row of this wave (steps
-    // outside are hidden from all of its rows: their P is 0, so skipping their products changes
-    // no bit of O or l).  The wave still takes part in those steps' copies and barriers.
+    // Window and causal instances: the steps that hold a key visible to some row of this wave
+    // (steps outside are hidden from all of its rows: their P is 0, so skipping their products
+    // changes no bit of O or l).  The wave still takes part in those steps' copies and barriers.
+    // Causal: the workgroup's last four steps cross the diagonal, and wave w's rows see only
+    // the first w + 1 of them.
     int jact_lo = 0, jact_hi = 1 << 30;
     if constexpr (WIN) {
         if (wl >= 0) jact_lo = max(0, (q0 - wl - kb) / kBC);
@@ -349,8 +351,9 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
         jact_hi = min(jact_hi, Lr > 0 ? (Lr - 1) / kBC : -1);
         if (wr >= 0 && q0 + kWR - 1 + wr - kb < 0) jact_hi = -1;
     }
+    if constexpr (CAUSAL) jact_hi = (q0 + kWR - 1) / kBC;
     auto active = [&](auto maskn, int jj) {   // (unmasked steps are always active)
-        if constexpr (WIN && decltype(maskn)::value) return jj >= jact_lo && jj <= jact_hi;
+        if constexpr ((WIN || CAUSAL) && decltype(maskn)::value) return jj >= jact_lo && jj <= jact_hi;
         else return true;
     };
     auto step = [&](auto maskn, auto odd, auto ph, int j, f32x16 (&cur)[NH][kNT],
