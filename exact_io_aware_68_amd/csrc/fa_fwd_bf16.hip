@@ -24,9 +24,11 @@
 //     exponentiates step j; the MFMAs of P(j) V(j) run while the VALU takes the row max of
 //     S(j+1).  The interleaving itself is left to the compiler's scheduler, which measured
 //     faster than a hand-fenced order (one MFMA per fence, operands read one MFMA ahead).
-//   * The kernel is templated on NH, 32-row query halves per wave; the built instances use
-//     NH = 1 (two waves per SIMD): NH = 2 halves the LDS reads per flop but needs more
-//     registers than two waves per SIMD allow and measured slower at one wave per SIMD.
+//   * The kernel is templated on NH, 32-row query halves per wave.  NH = 2 halves the LDS reads
+//     per flop; with d = 128 (or causal, d = 64) it needs more registers than two waves per
+//     SIMD allow and measured slower at one wave per SIMD, so those instances use NH = 1.  The
+//     non-causal d = 64 instance fits NH = 2 in 252 registers (two waves per SIMD) and takes
+//     it: 256-row workgroups, half as many.
 //   * Scores are kept in log2 units: 2^(s * scale * log2 e - m) uses one FMA and v_exp_f32.
 //     The reference point m is the first step's row max and moves only when a step's P would
 //     sum past 2^16 in some lane, so the common step computes no row max at all; this is exact
@@ -71,8 +73,8 @@ struct FwdLds {
 
 }  // namespace
 
-// NH = 32-row query halves per wave: 1 -> 128-row workgroups, 2 waves per SIMD; 2 -> 256-row
-// workgroups, one wave per SIMD, every LDS fragment feeding two MFMAs.
+// NH = 32-row query halves per wave: 1 -> 128-row workgroups; 2 -> 256-row workgroups, every
+// LDS fragment feeding two MFMAs.
 template <int NH>
 constexpr int rows_per_block() { return kWaves * 32 * NH; }
 
@@ -342,8 +344,8 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
     // Window and causal instances: the steps that hold a key visible to some row of this wave
     // (steps outside are hidden from all of its rows: their P is 0, so skipping their products
     // changes no bit of O or l).  The wave still takes part in those steps' copies and barriers.
-    // Causal: the workgroup's last four steps cross the diagonal, and wave w's rows see only
-    // the first w + 1 of them.
+    // Causal (NH = 1): the workgroup's last four steps cross the diagonal, and wave w's rows
+    // see only the first w + 1 of them.
     int jact_lo = 0, jact_hi = 1 << 30;
     if constexpr (WIN) {
         if (wl >= 0) jact_lo = max(0, (q0 - wl - kb) / kBC);
@@ -472,11 +474,13 @@ __global__ __launch_bounds__(kThreads, kWindowWavesPerSimd) void fwd_window_bf16
     fwd_bf16_body<D, false, NH, true>(p);
 }
 
-// Halves per wave of the built instances.
+// Halves per wave of the built instances: kNH, except the non-causal d = 64 instance (kNH64).
 constexpr int kNH = 1;
+constexpr int kNH64 = 2;
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-    constexpr int kBR = rows_per_block<kNH>();
+    const bool wide = p.d == 64 && !p.causal;   // the kNH64 instance
+    const int kBR = wide ? rows_per_block<kNH64>() : rows_per_block<kNH>();
     const int nqt = (p.N + kBR - 1) / kBR;
     dim3 grid((unsigned)((long long)nqt * p.Hq * p.B)), block(kThreads);
     if (p.d == 128) {
@@ -488,7 +492,7 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
         if (p.causal)
             hipLaunchKernelGGL((fwd_bf16_kernel<64, true, kNH>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((fwd_bf16_kernel<64, false, kNH>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((fwd_bf16_kernel<64, false, kNH64>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
 }
