@@ -82,6 +82,10 @@ CASES = [  # (B, Hq, Hkv, N, d, causal, padded)
     (1, 8, 8, 640, 128, True, False),
     (1, 4, 4, 768, 128, True, False),
     (1, 16, 4, 512, 128, True, True),
+    # the non-causal d = 64 instance takes 256-row workgroups: several of them with a ragged
+    # last one, grouped-query heads and key lengths
+    (2, 6, 2, 700, 64, False, True),
+    (1, 3, 3, 513, 64, False, False),
 ]
 
 
@@ -95,9 +99,10 @@ def test_bf16_parity_small(B, Hq, Hkv, N, d, causal, padded):
     check_close("LSE", np64(lse), LSE, TOL_LSE)
 
 
-def test_bf16_key_lengths_edge_values():
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_key_lengths_edge_values(d):
     """key_lens of 0 (row has no key: O = 0, LSE = -inf), 1, a tile edge and N."""
-    x = gen(4, 2, 1, 200, 128, "bf16", 7)
+    x = gen(4, 2, 1, 200, d, "bf16", 7)
     x["key_lens"] = torch.tensor([0, 1, 64, 200], dtype=torch.int32)
     for causal in (False, True):
         o, lse = run_fwd(x, causal)
@@ -110,23 +115,25 @@ def test_bf16_key_lengths_edge_values():
 def test_nan_padding_never_reaches_outputs():
     x = gen(2, 2, 2, 256, 64, "bf16", 8)
     x["key_lens"] = torch.tensor([100, 193], dtype=torch.int32)
-    o_ref, l_ref = run_fwd(x, True)
+    refs = [run_fwd(x, causal) for causal in (False, True)]
     for b, L in enumerate([100, 193]):
         x["k"][b, :, L:] = float("nan")
         x["v"][b, :, L:] = float("nan")
-    o, lse = run_fwd(x, True)
-    assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+    for causal, (o_ref, l_ref) in zip((False, True), refs):
+        o, lse = run_fwd(x, causal)
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
 
 
-def test_every_output_written_and_canaries_intact():
-    x = gen(2, 2, 1, 190, 128, "bf16", 9)
+@pytest.mark.parametrize("d,causal", [(128, True), (64, False)])
+def test_every_output_written_and_canaries_intact(d, causal):
+    x = gen(2, 2, 1, 190, d, "bf16", 9)
     q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
     n_o, n_l = q.numel(), 2 * 2 * 190
     ob = torch.full((n_o + 2048,), float("nan"), dtype=torch.bfloat16, device=DEV)
     lb = torch.full((n_l + 2048,), float("nan"), dtype=torch.float32, device=DEV)
     o = ob[1024:1024 + n_o].view(q.shape)
     lse = lb[1024:1024 + n_l].view(2, 2, 190)
-    fa.fa_fwd(q, k, v, scale=x["scale"], causal=True, o=o, lse=lse)
+    fa.fa_fwd(q, k, v, scale=x["scale"], causal=causal, o=o, lse=lse)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
     assert torch.isnan(ob[:1024]).all() and torch.isnan(ob[1024 + n_o:]).all()
