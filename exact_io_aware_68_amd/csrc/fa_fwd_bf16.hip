@@ -229,14 +229,14 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
             float pe[kNT][16];
             float rs;
             auto expo = [&]() {
-                const float muse = m[h] == kNegInf ? 0.f : m[h];
-                rs = 0.f;
+                // Only window rows can still lack a reference point (-inf) here.
+                const float muse = (WIN && m[h] == kNegInf) ? 0.f : m[h];
 #pragma unroll
                 for (int t = 0; t < kNT; ++t)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         pe[t][r] = exp2_hw(__builtin_fmaf(st[h][t][r], C, -muse));
-                        rs += pe[t][r];
+                        rs = (t == 0 && r == 0) ? pe[0][0] : rs + pe[t][r];
                     }
             };
             if (fresh) {
