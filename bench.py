@@ -41,7 +41,7 @@ KERNEL_SRC = {                 # kernel -> sources whose hash guards stored coun
     "bwd_dq": [_CSRC + "fa_bwd_dq.hip", _CSRC + "fa_device.h"],
     "splitkv": [_CSRC + "fa_splitkv.hip", _CSRC + "fa_device.h"],
     "fwd_window": [_CSRC + "fa_fwd_bf16.hip", _CSRC + "fa_device.h"],
-    "fwd_sparse": [_CSRC + "fa_fwd_sparse.hip", _CSRC + "fa_device.h"],
+    "fwd_sparse": [_CSRC + "fa_fwd_bf16.hip", _CSRC + "fa_device.h"],
     "splitkv_merge": [_CSRC + "fa_splitkv.hip", _CSRC + "fa_device.h"],
 }
 # rocprofv3 kernel-name fragment -> kernel key

@@ -30,8 +30,8 @@ bool grid_fits(long double blocks, int threads) {
 }
 long double tiles(int n, int t) { return (long double)((n + (long long)t - 1) / t); }
 
-// Workgroup counts of the launches (kernel files: fa_fwd_bf16.hip, fa_fwd_f32.hip,
-// fa_fwd_sparse.hip, fa_bwd_bf16.hip, fa_bwd_dq.hip, fa_splitkv.hip).
+// Workgroup counts of the launches (kernel files: fa_fwd_bf16.hip with the dense, window and
+// block-sparse forwards, fa_fwd_f32.hip, fa_bwd_bf16.hip, fa_bwd_dq.hip, fa_splitkv.hip).
 bool fwd_grid_fits(int B, int Hq, int N, fa_dtype dtype) {
     if (dtype == FA_F32) return grid_fits((long double)B * Hq * tiles(N, 64), 64);
     return grid_fits((long double)B * Hq * tiles(N, 128), 256);

@@ -37,6 +37,10 @@
 //     cannot leak through 0 * NaN in P V, and are masked to -inf before the max.
 //   * Causal: tiles entirely above the diagonal are never loaded; only diagonal and tail steps
 //     are masked; query tiles of a head run longest first; XCD-aware workgroup order.
+//   * The same body serves the local-window instances (WIN) and the block-sparse ones (LIST:
+//     the key tiles come from a list of the bitmap row's active tiles).
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -71,6 +75,14 @@ struct FwdLds {
     bf16 v[2][kLT * D];   // swizzled V tiles
 };
 
+constexpr int kMaxTiles = 1024;   // block-sparse: 64-key tiles per bitmap row (N <= 65536)
+
+template <int D>
+struct FwdListLds : FwdLds<D> {
+    short act[kMaxTiles];   // block-sparse: active key tiles of the workgroup's bitmap row
+    int nact, nfree;        // list length; leading entries that need no mask
+};
+
 }  // namespace
 
 // NH = 32-row query halves per wave: 1 -> 128-row workgroups; 2 -> 256-row workgroups, every
@@ -81,13 +93,20 @@ constexpr int rows_per_block() { return kWaves * 32 * NH; }
 // WIN: local-window instance (tutorial page, "Other Efficient Attention Variants", Local
 // Attention Window): row i sees keys i - wl .. i + wr; the workgroup visits only the key tiles
 // its rows' windows overlap (O(N w) work), and masks every step.
-template <int D, bool CAUSAL, int NH, bool WIN>
+// LIST: block-sparse instance (study-note page, "FlashAttention paper", What it does not
+// claim): the workgroup visits only the 64-key tiles its row of the bitmap p.block_mask marks
+// active.  Wave 0 compacts that row into an ascending list in LDS; step j then covers keys
+// 64 act[j/2] + 32 (j%2) .., and the shifted K tile T holds the second half of entry T and the
+// first half of entry T+1 (two 32-row copies), so the loop below is the same as the dense one.
+template <int D, bool CAUSAL, int NH, bool WIN, bool LIST = false>
 __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
+    static_assert(!(WIN && LIST), "a window and a block bitmap are separate instances");
     constexpr int kBR = rows_per_block<NH>();
     constexpr int kWR = 32 * NH;
     constexpr int NS = D / 16;      // reduction steps of Q K^T
     constexpr int ND = D / 32;      // 32-column blocks of O
-    __shared__ __attribute__((aligned(1024))) FwdLds<D> sm;
+    using Lds = typename std::conditional<LIST, FwdListLds<D>, FwdLds<D>>::type;
+    __shared__ __attribute__((aligned(1024))) Lds sm;
 
     const int tid = threadIdx.x;
     // The wave index is uniform across the wave; saying so keeps the DMA addresses derived from
@@ -146,7 +165,55 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
         if (wr >= 0) kend = min(kend, qt * kBR + kBR + wr);
     }
     kend = max(kend - kb, 0);                    // relative to kb from here on
-    const int ntiles = (kend + kBC - 1) / kBC;
+
+    // Block-sparse: active key tiles below kend, compacted by wave 0.  Lane t of each 64-tile
+    // chunk holds tile c0 + t; ballot and a lane prefix count give its list position.  A tile
+    // needs no mask when all its keys lie below Lk and (causal) at or below the workgroup's
+    // first row; the list is ascending and both masks hide only high keys, so those tiles are
+    // a prefix of it.
+    if constexpr (LIST) {
+        if (w == 0) {
+            const int ntl = (kend + kLT - 1) / kLT;
+            const uint8_t* row = p.block_mask + (size_t)qt * ((N + kLT - 1) / kLT);
+            const int free_end = CAUSAL ? min(Lk, qt * kBR + 1) : Lk;   // keys below: unmasked
+            int base = 0, nfree = 0;
+            for (int c0 = 0; c0 < ntl; c0 += 64) {
+                const int t = c0 + lane;
+                const bool on = t < ntl && row[t] != 0;
+                const uint64_t bits = __builtin_amdgcn_ballot_w64(on);
+                const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                           (uint32_t)(bits >> 32),
+                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0u));
+                if (on) sm.act[pos] = (short)t;
+                const uint64_t freebits =
+                    __builtin_amdgcn_ballot_w64(on && (t + 1) * kLT <= free_end);
+                base += __builtin_popcountll(bits);
+                nfree += __builtin_popcountll(freebits);
+            }
+            if (lane == 0) {
+                sm.nact = base;
+                sm.nfree = nfree;
+            }
+        }
+        __syncthreads();
+    }
+    int nact = 0;   // block-sparse list length
+    if constexpr (LIST) nact = __builtin_amdgcn_readfirstlane(sm.nact);
+    const int ntiles = LIST ? 2 * nact : (kend + kBC - 1) / kBC;
+    // First key of list entry T (block-sparse) and of step j (relative to kb otherwise).
+    auto tile_key = [&](int T) {
+        if constexpr (LIST) return __builtin_amdgcn_readfirstlane((int)sm.act[T]) * kLT;
+        else return T * kLT;
+    };
+    auto step_key = [&](int j) {
+        if constexpr (LIST) return tile_key(j >> 1) + (j & 1) * kBC;
+        else return kb + j * kBC;
+    };
+    // Steps below jfree need no mask for any row of the workgroup (not used by window
+    // instances, whose loops take their own bounds).
+    int jfree = Lk / kBC;
+    if (CAUSAL) jfree = min(jfree, (qt * kBR + 1) / kBC);
+    if constexpr (LIST) jfree = 2 * __builtin_amdgcn_readfirstlane(sm.nfree);
 
     f32x16 oacc[NH][ND];
     float m[NH];      // running max of scaled scores, log2 units
@@ -188,14 +255,14 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
             }
     };
     auto need_mask = [&](int j) {   // some key of step j hidden from some row of the wave
-        const int k0 = kb + j * kBC;
+        const int k0 = step_key(j);
         bool cut = (CAUSAL && k0 + kBC - 1 > q0) || (k0 + kBC > Lk);
         if constexpr (WIN)
             cut = cut || (wr >= 0 && k0 + kBC - 1 > q0 + wr) || (wl >= 0 && k0 < q0 + kWR - 1 - wl);
         return cut;
     };
     auto mask = [&](int j, f32x16 (&st)[NH][kNT]) {
-        const int k0 = kb + j * kBC;
+        const int k0 = step_key(j);
 #pragma unroll
         for (int h = 0; h < NH; ++h)
 #pragma unroll
@@ -299,22 +366,33 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
         return sm.k[((j - 1) >> 1) & 1] + ((j - 1) & 1) * kBC * D;
     };
     auto vsub = [&](int j) { return sm.v[(j >> 1) & 1] + (j & 1) * kBC * D; };
-    const int nlt = (kend + kLT - 1) / kLT;                       // V tiles
-    const int nkt = kend > kBC ? (kend - kBC + kLT - 1) / kLT : 0;  // shifted K tiles
+    // V tiles and shifted K tiles (block-sparse: one of each per list entry)
+    const int nlt = LIST ? nact : (kend + kLT - 1) / kLT;
+    const int nkt = LIST ? nact : (kend > kBC ? (kend - kBC + kLT - 1) / kLT : 0);
     const bf16* __restrict__ Kr = K + (size_t)kb * D;
     const bf16* __restrict__ Vr = V + (size_t)kb * D;
     auto load_k = [&](int T, int buf) {   // shifted K tile T: keys kb + 64 T + 32 .. + 95
-        const int k0 = T * kLT + kBC;
-        dma_tile<D, kLT, kWaves>(Kr + (size_t)k0 * D, Lr - k0, sm.k[buf], w, lane);
+        if constexpr (LIST) {   // the second half of entry T, then the first half of entry T+1
+            const int k0 = tile_key(T) + kBC;
+            dma_tile<D, kBC, kWaves>(K + (size_t)k0 * D, Lk - k0, sm.k[buf], w, lane);
+            if (T + 1 < nact) {
+                const int k1 = tile_key(T + 1);
+                dma_tile<D, kBC, kWaves>(K + (size_t)k1 * D, Lk - k1, sm.k[buf] + kBC * D, w, lane);
+            }
+        } else {
+            const int k0 = T * kLT + kBC;
+            dma_tile<D, kLT, kWaves>(Kr + (size_t)k0 * D, Lr - k0, sm.k[buf], w, lane);
+        }
     };
     auto load_v = [&](int T, int buf) {
-        const int k0 = T * kLT;
+        const int k0 = tile_key(T);
         dma_tile<D, kLT, kWaves>(Vr + (size_t)k0 * D, Lr - k0, sm.v[buf], w, lane);
     };
     f32x16 sa[NH][kNT], sb[NH][kNT];
     bf16x8 pf[NH][kNT][2];
-    if (ntiles > 0) {
-        dma_tile<D, kBC, kWaves>(Kr, Lr, sm.k[1] + kBC * D, w, lane);   // keys kb .. kb + 31
+    if (ntiles > 0) {   // keys of step 0 (kb .. kb + 31)
+        const int k0 = tile_key(0);
+        dma_tile<D, kBC, kWaves>(Kr + (size_t)k0 * D, Lr - k0, sm.k[1] + kBC * D, w, lane);
         load_v(0, 0);
         if (nkt > 0) load_k(0, 0);
     }
@@ -323,9 +401,12 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
     if (ntiles > 0) {
         scores(ksub(0), sa);
         if (need_mask(0)) mask(0, sa);
-        // Without a window every row sees key 0 in step 0, so the reference point starts at
-        // step 0's row max (finite: every later rescale is a finite factor).  Window instances
-        // leave it unset; their first steps set it (see exponentiate).
+        // Without a window a row that sees any key sees the first key of step 0 (the causal
+        // mask and the key length hide only keys above a bound of the row; a block-sparse list
+        // is ascending), so the reference point starts at step 0's row max (finite: every
+        // later rescale is a finite factor); a row that sees no key at all keeps P = 0 under
+        // any point.  Window instances leave it unset; their first steps set it (see
+        // exponentiate).
         if constexpr (!WIN) {
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
@@ -354,8 +435,12 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
         if (wr >= 0 && q0 + kWR - 1 + wr - kb < 0) jact_hi = -1;
     }
     if constexpr (CAUSAL) jact_hi = (q0 + kWR - 1) / kBC;
+    int klast = Lk - 1;   // block-sparse: the last key some row of the wave sees
+    if (CAUSAL) klast = min(klast, q0 + kWR - 1);
     auto active = [&](auto maskn, int jj) {   // (unmasked steps are always active)
-        if constexpr ((WIN || CAUSAL) && decltype(maskn)::value) return jj >= jact_lo && jj <= jact_hi;
+        if constexpr (LIST && decltype(maskn)::value) return step_key(jj) <= klast;
+        else if constexpr ((WIN || CAUSAL) && decltype(maskn)::value)
+            return jj >= jact_lo && jj <= jact_hi;
         else return true;
     };
     auto step = [&](auto maskn, auto odd, auto ph, int j, f32x16 (&cur)[NH][kNT],
@@ -408,9 +493,6 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
             step(Flag<true>{}, Flag<true>{}, Phase<-1>{}, j + 1, sb, sa);
         }
     } else {
-        // Steps below jfree need no mask for any row of the workgroup.
-        int jfree = Lk / kBC;
-        if (CAUSAL) jfree = min(jfree, (qt * kBR + 1) / kBC);
         // j is a multiple of 4 in this loop: fixed buffers, constant LDS addresses
         for (; j + 4 < ntiles && j + 4 < jfree; j += 4) {
             step(Flag<false>{}, Flag<false>{}, Phase<0>{}, j, sa, sb);
@@ -474,6 +556,12 @@ __global__ __launch_bounds__(kThreads, kWindowWavesPerSimd) void fwd_window_bf16
     fwd_bf16_body<D, false, NH, true>(p);
 }
 
+// Block-sparse instances: 128-row workgroups (one bitmap row each).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void fwd_sparse_bf16_kernel(FwdParams p) {
+    fwd_bf16_body<D, CAUSAL, 1, false, true>(p);
+}
+
 // Halves per wave of the built instances: kNH, except the non-causal d = 64 instance (kNH64).
 constexpr int kNH = 1;
 constexpr int kNH64 = 2;
@@ -506,6 +594,25 @@ hipError_t launch_fwd_window_bf16(const FwdParams& p, hipStream_t stream) {
         hipLaunchKernelGGL((fwd_window_bf16_kernel<128, kNH>), grid, block, 0, stream, p);
     else
         hipLaunchKernelGGL((fwd_window_bf16_kernel<64, kNH>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+// Block-sparse instances (fa_fwd_blocksparse).
+hipError_t launch_fwd_sparse_bf16(const FwdParams& p, hipStream_t stream) {
+    constexpr int kBR = rows_per_block<1>();
+    const int nqt = (p.N + kBR - 1) / kBR;
+    dim3 grid((unsigned)((long long)nqt * p.Hq * p.B)), block(kThreads);
+    if (p.d == 128) {
+        if (p.causal)
+            hipLaunchKernelGGL((fwd_sparse_bf16_kernel<128, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((fwd_sparse_bf16_kernel<128, false>), grid, block, 0, stream, p);
+    } else {
+        if (p.causal)
+            hipLaunchKernelGGL((fwd_sparse_bf16_kernel<64, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((fwd_sparse_bf16_kernel<64, false>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 
