@@ -457,8 +457,11 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdParams& p) {
         const bool act_j = active(maskn, j), act_n = active(maskn, j + 1);
         if (act_n) scores(sm.k[tb] + half * kBC * D, nxt);  // MFMA (= ksub(j + 1)) ...
         if (act_j) exponentiate(j, cur, pf);                // ... alongside VALU
-        if constexpr (decltype(maskn)::value)
-            if (act_n) mask(j + 1, nxt);
+        if constexpr (decltype(maskn)::value) {
+            // Window instances mask a step only where it hides a key from a row of this wave
+            // (each edge cuts about two of a wave's steps, four of the workgroup's).
+            if (act_n && (!WIN || need_mask(j + 1))) mask(j + 1, nxt);
+        }
         if (act_j) pv(sm.v[tb] + half * kBC * D, pf);       // (= vsub(j))
         if constexpr (decltype(odd)::value) {
             wait_vmem();       // this wave's share of tiles T+1 has landed
