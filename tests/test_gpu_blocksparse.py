@@ -137,3 +137,38 @@ def test_sparse_past_2_31_elements():
     check_close("LSE", np64(lse[idx]), LSE, TOL_LSE)
     del x, o, lse
     torch.cuda.empty_cache()
+
+
+def test_causal_rows_whose_only_block_lies_past_them():
+    """Causal, one active block on the diagonal: the first half of that row block's rows sees no
+    key at all (O = 0, LSE = -inf) and its waves skip every step; the rest see part of it."""
+    x = gen(1, 2, 2, 384, 128, 43)
+    bm = torch.zeros(3, 6, dtype=torch.uint8)
+    bm[1, 3] = 1                   # rows 128..255: keys 192..255, visible to rows >= 192 only
+    bm[2, 2] = 1                   # rows 256..383: keys 128..191, visible to all of them
+    o, lse = run(x, bm, True)
+    check(x, bm, True, o, lse)
+    assert torch.all(o[:, :, 128:192] == 0) and torch.all(torch.isneginf(lse[:, :, 128:192]))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_very_negative_logits(causal):
+    """Every scaled logit near -150 in log2 units (K close to -Q), with sparse rows whose first
+    active block is far from key 0: exponentials taken against any reference point other than a
+    visible score's would underflow fp32."""
+    B, Hq, Hkv, N, d = 1, 2, 1, 640, 128
+    scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    a = (150.0 / (scale * 1.4426950408889634 * d)) ** 0.5
+    g = torch.Generator().manual_seed(97 + causal)
+    q = (a + 0.1 * a * torch.randn(B, Hq, N, d, generator=g)).to(torch.bfloat16)
+    k = (-a + 0.1 * a * torch.randn(B, Hkv, N, d, generator=g)).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16)
+    x = {"q": q, "k": k, "v": v, "scale": scale, "key_lens": None}
+    bm = (torch.rand(5, 10, generator=g) < 0.4).to(torch.uint8)
+    bm[:, :3] = 0                  # no row block sees keys 0..191
+    bm[1:, 3] = 1
+    o, lse = run(x, bm, causal)
+    O, LSE = attn_fwd(q, k, v, scale, causal, None, block_mask=(bm.numpy(), fa.BLOCK_Q, fa.BLOCK_K))
+    rows = np.isfinite(LSE)
+    assert np.median(LSE[rows]) < -90.0
+    check(x, bm, causal, o, lse)
