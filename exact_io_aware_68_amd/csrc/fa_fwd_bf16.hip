@@ -92,7 +92,7 @@ constexpr int rows_per_block() { return kWaves * 32 * NH; }
 
 // WIN: local-window instance (tutorial page, "Other Efficient Attention Variants", Local
 // Attention Window): row i sees keys i - wl .. i + wr; the workgroup visits only the key tiles
-// its rows' windows overlap (O(N w) work), and masks every step.
+// its rows' windows overlap (O(N w) work), and masks only the steps at the windows' edges.
 // LIST: block-sparse instance (study-note page, "FlashAttention paper", What it does not
 // claim): the workgroup visits only the 64-key tiles its row of the bitmap p.block_mask marks
 // active.  Wave 0 compacts that row into an ascending list in LDS; step j then covers keys
