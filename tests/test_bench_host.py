@@ -108,3 +108,11 @@ def test_causal_pairs_with_key_lengths():
         i, j = np.arange(N)[:, None], np.arange(N)[None, :]
         assert bench.causal_pairs(N, L) == int(((j <= i) & (j < L)).sum())
     assert bench.causal_pairs(8, 8) == 8 * 9 // 2
+
+
+def test_every_kernel_source_the_traffic_guard_hashes_exists():
+    """The stored counter rows are tied to these files: a missing one would silently change the
+    hash rather than fail."""
+    for kernel, files in bench.KERNEL_SRC.items():
+        for f in files:
+            assert os.path.isfile(os.path.join(ROOT, f)), (kernel, f)
