@@ -181,14 +181,20 @@ def test_scores_rising_and_falling_along_keys(causal, d):
 
 # ------------------------------------------------------------------ full-size workloads
 
-def _sample_rows(w, n_rand, seed):
+def _sample_rows(w, n_rand, seed, key_lens=None):
+    """Tile and sequence edges of every (batch, q-head) (the rows around each batch's key length
+    included), more edges of the first and last q-head, and n_rand random rows."""
     r = np.random.default_rng(seed)
     picks = set()
     for b in range(w.B):
+        L = w.N if key_lens is None else int(key_lens[b])
+        edges = {0, 127, 128, L - 1, L, L + 1, w.N - 1}
+        for h in range(w.Hq):
+            picks.update((b, h, i) for i in edges if 0 <= i < w.N)
         for h in (0, w.Hq - 1):
-            for i in (0, 1, 63, 64, 127, 128, w.N // 2, w.N - 2, w.N - 1):
-                picks.add((b, h, i))
-    while len(picks) < n_rand + 36 * w.B:
+            picks.update((b, h, i) for i in (1, 63, 64, w.N // 2, w.N - 2))
+    n0 = len(picks)
+    while len(picks) < n0 + n_rand:
         picks.add((int(r.integers(w.B)), int(r.integers(w.Hq)), int(r.integers(w.N))))
     return sorted(picks)
 
@@ -197,13 +203,15 @@ def _sample_rows(w, n_rand, seed):
 def test_full_size_workload_sampled_rows(name):
     """Rows of every q-head of the largest workload, beyond the head subset that
     tests/test_gpu_full_parity.py checks in full: the oracle recomputes sampled rows one by one
-    (first, last, tile edges, random) and every row is checked for finiteness."""
+    (first, last, tile edges and the rows around each batch's key length of every q-head, plus
+    random rows) and every row is checked for finiteness."""
     w = fi.WORKLOADS[name]
     print(f"\nfull-size {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d}", flush=True)
     x = fi.make(w)
     o, lse = run_fwd(x, w.causal)
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
-    picks = _sample_rows(w, 96, w.seed)
+    picks = _sample_rows(w, 96, w.seed, x["key_lens"])
+    assert {(b, h) for b, h, _ in picks} == {(b, h) for b in range(w.B) for h in range(w.Hq)}
     O, LSE = attn_fwd_rows(x["q"], x["k"], x["v"], x["scale"], w.causal, x["key_lens"], picks)
     idx = tuple(torch.tensor(a) for a in zip(*picks))
     check_close("O", np64(o[idx]), O, TOL_BF16_MAX, TOL_BF16_MEAN)
