@@ -7,6 +7,8 @@ Exact, not approximate).  So every row of the bf16 workloads is compared with th
   - c2 (B=4 H=16 N=2048 d=64, non-causal): O and LSE of all 64 heads;
   - c3 (B=2 H=16 N=8192 d=128, causal): O and LSE of all 32 heads;
   - c5 (B=2 H=16 N=4096 d=128, causal backward): dQ, dK, dV of all 32 heads;
+  - the local-window workload (B=2 H=16 N=8192 d=128, window (512, 512)) and the block-sparse
+    workload (same shape, its bitmap): O and LSE of all 32 heads;
   - c4 (B=4 Hq=32 Hkv=8 N=16384 d=128, causal, key lengths): a stated subset of 32 q-heads,
     one per (batch, kv-group): q-head g*4 + (b + g) % 4 of kv-group g in batch b, so every batch
     (every key length), every kv-group and every position inside a group is covered.  The other
@@ -34,30 +36,47 @@ def c4_heads(w):
     return [(b, g * G + (b + g) % G) for b in range(w.B) for g in range(w.Hkv)]
 
 
-def forward_full(name, heads=None):
-    w = fi.WORKLOADS[name]
+def forward_full(name, heads=None, window=None, bitmap=None):
+    """Every row of the named workload's heads (all, or the given (b, h) subset) against the
+    oracle: the dense forward, or the local-window / block-sparse forward on that workload's
+    window or bitmap."""
+    if window is not None:
+        w, _ = fi.WINDOW_WORKLOADS[name]
+    elif bitmap is not None:
+        w, _ = fi.SPARSE_WORKLOADS[name]
+    else:
+        w = fi.WORKLOADS[name]
     x = fi.make(w)
     q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
     kl = None if x["key_lens"] is None else x["key_lens"].to(DEV)
-    o, lse = fa.fa_fwd(q, k, v, scale=x["scale"], causal=w.causal, key_lens=kl)
+    if window is not None:
+        o, lse = fa.fa_fwd_window(q, k, v, window=window, scale=x["scale"], key_lens=kl)
+    elif bitmap is not None:
+        o, lse = fa.fa_fwd_blocksparse(q, k, v, bitmap.to(DEV), scale=x["scale"],
+                                       causal=w.causal, key_lens=kl)
+    else:
+        o, lse = fa.fa_fwd(q, k, v, scale=x["scale"], causal=w.causal, key_lens=kl)
     torch.cuda.synchronize()
     o, lse = o.cpu(), lse.cpu()
     G = w.Hq // w.Hkv
     heads = heads or [(b, h) for b in range(w.B) for h in range(w.Hq)]
     lens = None if x["key_lens"] is None else x["key_lens"].tolist()
+    bm = None if bitmap is None else (bitmap.numpy(), fa.BLOCK_Q, fa.BLOCK_K)
 
     def ref(bh):
         b, h = bh
         g = h // G
         return attn_fwd(x["q"][b:b + 1, h:h + 1], x["k"][b:b + 1, g:g + 1],
                         x["v"][b:b + 1, g:g + 1], x["scale"], w.causal,
-                        None if lens is None else [lens[b]])
+                        None if lens is None else [lens[b]], window=window, block_mask=bm)
 
     ao, al = Agg("O", TOL_BF16_MAX, TOL_BF16_MEAN), Agg("LSE", TOL_LSE)
     t0 = time.time()
     for (b, h), (O, LSE) in zip(heads, oracle_map(ref, heads)):
+        rows = np.isfinite(LSE[0, 0])   # rows with no visible key: O = 0 and LSE = -inf
+        assert np.all(np.isneginf(np64(lse[b, h])[~rows])) and np.all(np64(o[b, h])[~rows] == 0)
         ao.add(np64(o[b, h]), O[0, 0])
-        al.add(np64(lse[b, h]), LSE[0, 0])
+        al.add(np64(lse[b, h])[rows], LSE[0, 0][rows])
     (om, omean), (lm, _) = ao.check(), al.check()
     print(f"\n{name}: {len(heads)} heads, {ao.n} O elements; O max {om:.3g} mean {omean:.3g}, "
           f"LSE max {lm:.3g} (oracle {time.time() - t0:.1f} s)", flush=True)
@@ -68,6 +87,20 @@ def test_forward_every_row(name):
     w = fi.WORKLOADS[name]
     print(f"\nfull parity {name}: B={w.B} Hq={w.Hq} N={w.N} d={w.d} causal={w.causal}", flush=True)
     forward_full(name)
+
+
+def test_window_every_row():
+    w, win = fi.WINDOW_WORKLOADS["window"]
+    print(f"\nfull parity window: B={w.B} H={w.Hq} N={w.N} d={w.d} window={win}", flush=True)
+    forward_full("window", window=win)
+
+
+def test_sparse_every_row():
+    w, density = fi.SPARSE_WORKLOADS["sparse"]
+    bm = fi.block_bitmap(w.N, density, w.seed)
+    print(f"\nfull parity block-sparse: B={w.B} H={w.Hq} N={w.N} d={w.d}, {int(bm.sum())} of "
+          f"{bm.numel()} blocks", flush=True)
+    forward_full("sparse", bitmap=bm)
 
 
 def test_c4_forward_head_subset():
